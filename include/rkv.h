@@ -1,0 +1,238 @@
+/*
+ * rkv.h - C ABI of librkv: RadixAttention's prefix-shared KV cache on one
+ * AMD MI355X (gfx950).
+ *
+ * What the library does.  Requests that share a prompt prefix read the same
+ * cached K/V instead of recomputing it.  The KV cache is an LRU cache held in
+ * a radix tree over token sequences, with matching, insertion and eviction as
+ * its operations (unite.ai, "SGLang: Efficient Execution of Structured
+ * Language Model Programs", section "Introduccion a SGLang", RadixAttention
+ * bullet; the nine-step walkthrough in section "SGLang: Modelo de
+ * programacion y metodologia").  The K/V rows live in one token-slot pool;
+ * the tree hands out per-request index tables (req_to_token) that the GPU
+ * kernels use to gather those rows.
+ *
+ * Two halves:
+ *   host   - radix tree + FIFO slot allocator (C++; not thread-safe per
+ *            handle: drive one tree from one scheduler thread);
+ *   device - kv_scatter, attn_extend, attn_decode: hand-written HIP kernels
+ *            for gfx950, asynchronous on the caller's stream.
+ *
+ * Conventions for every call:
+ *   - Return value: RKV_OK (0) or a negative RKV_E* code.  No exception ever
+ *     crosses the ABI.  rkv_last_error() gives a thread-local message for the
+ *     last failure on the calling thread.
+ *   - Arguments are checked before any state changes; a call that returns
+ *     RKV_EINVAL has changed nothing (batch_prepare documents one exception).
+ *   - Counts and lengths are int64_t unless noted; slot ids are int32_t in
+ *     [0, pool_slots).
+ */
+#ifndef RKV_H
+#define RKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  RKV_OK = 0,
+  RKV_EINVAL = -1,   /* bad argument (null, negative, out of range, shape)   */
+  RKV_ENOSPC = -2,   /* not enough free slots                               */
+  RKV_EBUSY = -3,    /* eviction ran out of unlocked leaves                 */
+  RKV_EHIP = -4,     /* a HIP runtime call or kernel launch failed          */
+  RKV_ENOTSUP = -5   /* valid but unsupported shape or dtype                */
+};
+
+enum { RKV_F32 = 0, RKV_BF16 = 1 };
+
+typedef struct rkv_tree rkv_tree;
+
+/* Message for the last failing call on this thread ("" if none).  The pointer
+ * stays valid until the next rkv_* call on the same thread. */
+const char* rkv_last_error(void);
+
+/* Library version string, e.g. "rkv 0.1 gfx950". */
+const char* rkv_version(void);
+
+/* ------------------------------------------------------------------------
+ * Host: radix tree + slot allocator.
+ *
+ * State (the "contract" both this library and its test oracle follow):
+ *   node: id (root = 0, then a counter from 1 that never reuses ids), label
+ *   (tokens of the edge into the node), slots (one per label token), parent,
+ *   children keyed by first label token, last_access (tick), lock (count).
+ *   A global tick is incremented once at the start of every match and every
+ *   insert, and of nothing else.  The allocator is a FIFO of slot ids.
+ * ------------------------------------------------------------------------ */
+
+/* Creates a tree with an empty cache over a pool of `pool_slots` slots
+ * (1 <= pool_slots <= 2^31-1).  `initial_free`, if not NULL, gives the
+ * initial FIFO order and must be a permutation of [0, pool_slots) (EINVAL
+ * otherwise); NULL means 0, 1, ..., pool_slots-1.  *out receives the handle,
+ * owned by the caller until rkv_tree_destroy. */
+int rkv_tree_create(rkv_tree** out, int64_t pool_slots, const int32_t* initial_free);
+
+/* Frees the tree and everything it owns.  NULL is a no-op. */
+void rkv_tree_destroy(rkv_tree* t);
+
+/* Longest cached prefix of tok[0..n) (the page's "matching", Step 3 of the
+ * walkthrough: a new prompt finds its prefix and reuses its KV).  Walks from
+ * the root; where the query ends or diverges inside an edge, that edge is
+ * split (rkv contract: the new upper node gets a fresh id and copies the lower
+ * node's last_access and lock; the lower node keeps its id).  Every node on
+ * the path from the root to the stop node gets last_access = tick.
+ * Outputs: *out_len = matched length m, out_slots[0..m) = the cached slots in
+ * sequence order (out_slots must have room for n), *out_node = stop node id
+ * (0 when m = 0).  Slots stay owned by the tree and stay valid only while the
+ * stop node is locked. */
+int rkv_radix_match(rkv_tree* t, const int32_t* tok, int64_t n, int32_t* out_slots,
+                    int64_t* out_len, int64_t* out_node);
+
+/* lock: +1 on the lock count of `node` and every ancestor up to, not
+ * including, the root; locked nodes are never evicted.  unlock: -1 on the
+ * same nodes; EINVAL (and no change) if any count would go negative or the
+ * node does not exist.  Node 0 (the root) is a no-op for both. */
+int rkv_radix_lock(rkv_tree* t, int64_t node);
+int rkv_radix_unlock(rkv_tree* t, int64_t node);
+
+/* Inserts tok[0..n) with the caller's slots[0..n) (walkthrough Steps 2-3: a
+ * finished sequence enters the tree; the uncached rest becomes a new node).
+ * Walks and splits as match does.  The tree takes ownership of all n slots:
+ * for the m positions already cached the tree keeps its own slots and
+ * appends each caller slot that differs from the tree's to the FIFO tail, in
+ * increasing position; if m < n the rest becomes a new leaf (fresh id) under
+ * the stop node.  Every node on the path, the new leaf included, gets
+ * last_access = tick.  *out_cached = m.  Slots must be in [0, pool_slots). */
+int rkv_radix_insert(rkv_tree* t, const int32_t* tok, const int32_t* slots, int64_t n,
+                     int64_t* out_cached);
+
+/* LRU eviction (walkthrough Steps 5, 8, 9: whole nodes, least recently used
+ * first, under a memory limit).  While fewer than `want` tokens are freed:
+ * pick the unlocked non-root leaf with the smallest (last_access, id), append
+ * its slots to the FIFO tail in label order, detach it.  Whole leaves only,
+ * so *out_freed may exceed want.  Returns RKV_EBUSY if no candidate is left
+ * before `want` is reached; what was freed stays freed. */
+int rkv_radix_evict(rkv_tree* t, int64_t want, int64_t* out_freed);
+
+/* Pops n slots from the FIFO head into out[0..n).  RKV_ENOSPC, with no
+ * change, if fewer than n are free (no implicit eviction).  The caller owns
+ * the slots until it passes them to rkv_radix_insert or rkv_free. */
+int rkv_alloc(rkv_tree* t, int64_t n, int32_t* out);
+
+/* Appends slots[0..n) to the FIFO tail in the given order.  EINVAL if a
+ * slot is out of range or the FIFO would exceed pool_slots entries. */
+int rkv_free(rkv_tree* t, const int32_t* slots, int64_t n);
+
+/* out[8] = {cached tokens, free slots, evictable tokens (in nodes with lock
+ * 0), locked tokens, nodes (non-root), matched tokens over all prepared
+ * requests, prompt tokens over all prepared requests, evicted tokens}.
+ * Cache hit rate = out[5] / out[6]. */
+int rkv_stats(rkv_tree* t, int64_t out[8]);
+
+/* Canonical dump: DFS from the root, children in ascending first-token
+ * order; per node the int64 values (id, parent id (-1 for the root),
+ * last_access, lock, len, label[len], slots[len]).  Writes at most cap
+ * values; *len receives the full length (call with cap 0 to size). */
+int rkv_radix_serialize(rkv_tree* t, int64_t* buf, int64_t cap, int64_t* len);
+
+/* FIFO contents head to tail; same sizing convention as serialize. */
+int rkv_free_list(rkv_tree* t, int32_t* buf, int64_t cap, int64_t* len);
+
+/* Prepares one batch of B requests whose token ids are
+ * tok[tok_indptr[r] .. tok_indptr[r+1]) (lengths L_r >= 1, L_r <= ld).
+ * For r = 0..B-1 in order: match the first L_r - 1 tokens (so every request
+ * computes at least its last token), lock the stop node.  Then with
+ * T = sum(L_r - p_r): if fewer than T slots are free, evict the difference;
+ * on RKV_EBUSY unlock this batch's nodes and return RKV_EBUSY (the matches,
+ * splits, ticks and evictions already done remain).  Then pop T slots and
+ * give them to the requests in order, positions ascending.
+ * Outputs (host buffers owned by the caller):
+ *   req_to_token [B, ld] row-major: cached slots then new slots, -1 after L_r
+ *   prefix_lens[B] = p_r, seq_lens[B] = L_r, qo_indptr[B+1] = prefix sums of
+ *   n_r = L_r - p_r, new_slots[T] (new_cap must be >= sum L_r),
+ *   out_nodes[B] = locked stop nodes (hand them to rkv_batch_commit).
+ * B = 0 is a no-op. */
+int rkv_batch_prepare(rkv_tree* t, int32_t B, const int32_t* tok, const int64_t* tok_indptr,
+                      int32_t* req_to_token, int64_t ld, int32_t* prefix_lens,
+                      int32_t* seq_lens, int32_t* qo_indptr, int32_t* new_slots,
+                      int64_t new_cap, int64_t* out_nodes);
+
+/* Commits a prepared batch: for r = 0..B-1, insert the full sequence with
+ * slots req_to_token[r, 0..L_r), then unlock nodes[r]. */
+int rkv_batch_commit(rkv_tree* t, int32_t B, const int32_t* tok, const int64_t* tok_indptr,
+                     const int32_t* req_to_token, int64_t ld, const int64_t* nodes);
+
+/* ------------------------------------------------------------------------
+ * Device: every pointer below is a device pointer owned by the caller, 16-byte
+ * aligned, tensors contiguous.  Calls are asynchronous on `stream` (a
+ * hipStream_t; NULL = the null stream); the library allocates nothing on
+ * these paths except a 4-byte error flag per device the first time RKV_DEBUG
+ * is set, and never synchronizes except in that debug mode.
+ *
+ * Layouts: pools k_pool, v_pool are [pool_slots, Hkv, D] (one slot = Hkv*D
+ * contiguous elements); q and o are [rows, Hq, D]; req_to_token is int32
+ * [B, ld] row-major.  dtype is RKV_F32 or RKV_BF16 for q, pools and o alike.
+ * Supported: D in {64, 128}, Hq % Hkv == 0, Hq / Hkv <= 16; anything else is
+ * RKV_ENOTSUP.  Gathered slots are range-checked in the kernels: an entry
+ * outside [0, pool_slots) reads as zeros (scatter skips it) and, with the
+ * environment variable RKV_DEBUG=1, makes the call return RKV_EINVAL after a
+ * stream synchronization.
+ * ------------------------------------------------------------------------ */
+
+/* k_pool[slots[i]] = k_new[i] and v_pool[slots[i]] = v_new[i] for
+ * i in [0, T); k_new, v_new are [T, Hkv, D].  A plain copy: bit-exact, every
+ * other pool row untouched.  Slots must be distinct (duplicates race).  T = 0
+ * is a no-op. */
+int rkv_kv_scatter(const void* k_new, const void* v_new, const int32_t* slots, int64_t T,
+                   void* k_pool, void* v_pool, int64_t pool_slots, int32_t hkv, int32_t d,
+                   int32_t dtype, void* stream);
+
+/* Extend (prefill over a cached prefix).  Request r has p_r = prefix_lens[r]
+ * cached tokens and n_r = qo_indptr[r+1] - qo_indptr[r] new ones, whose
+ * queries are q rows qo_indptr[r] .. qo_indptr[r+1].  New row j sits at
+ * position c = p_r + j and attends causally to keys 0..c of its own request:
+ *   o[row, h] = sum_t softmax_t(sm_scale * q[row, h] . K_t) V_t,
+ *   K_t = k_pool[req_to_token[r, t], h / (Hq/Hkv)],  V_t likewise,
+ *   lse[row, h] = natural-log log-sum-exp of the scaled scores (fp32;
+ *   `lse` may be NULL).
+ * total_new must equal qo_indptr[B] (the number of q rows) and max_new must
+ * be >= every n_r; together they size the grid (a smaller max_new leaves rows
+ * of the longer requests unwritten).  The new tokens' K/V must already be in the pool (rkv_kv_scatter).
+ * bf16: QK^T and PV on bf16 MFMA with fp32 accumulation, fp32 online
+ * softmax, softmax weights rounded to bf16 for PV, o rounded to bf16 (RNE).
+ * f32: fp32 arithmetic throughout.  B = 0 or total_new = 0 is a no-op. */
+int rkv_attn_extend(const void* q, const void* k_pool, const void* v_pool, void* o, float* lse,
+                    const int32_t* req_to_token, int64_t ld, const int32_t* qo_indptr,
+                    const int32_t* prefix_lens, int32_t B, int64_t total_new, int32_t max_new,
+                    int32_t hq, int32_t hkv, int32_t d, float sm_scale, int32_t dtype,
+                    int64_t pool_slots, void* stream);
+
+/* Bytes of device workspace rkv_attn_decode needs for these sizes
+ * (num_splits as passed to rkv_attn_decode).  0 on bad arguments. */
+size_t rkv_attn_decode_workspace_bytes(int32_t B, int32_t hq, int32_t d, int32_t max_seq_len,
+                                       int32_t num_splits);
+
+/* Single-token decode: q, o are [B, Hq, D]; request r's query is its last
+ * position L_r - 1 (L_r = seq_lens[r] >= 1, its own K/V already scattered)
+ * and attends to all L_r keys req_to_token[r, 0..L_r) (same formula as
+ * extend).  Split-KV: the keys of a request are cut into S_r contiguous
+ * chunks, each reduced to a partial (max, sum, acc) in fp32, then merged by
+ * log-sum-exp rescaling.  S_r depends only on L_r and num_splits (0 = a
+ * fixed chunk of 512 keys; N > 0 = at most N chunks), never on the rest of
+ * the batch, so a request's output bits do not depend on its batch.  Every
+ * seq_lens[r] must be <= max_seq_len and <= ld.  `workspace` (ws_bytes >=
+ * rkv_attn_decode_workspace_bytes) holds the partials. */
+int rkv_attn_decode(const void* q, const void* k_pool, const void* v_pool, void* o, float* lse,
+                    const int32_t* req_to_token, int64_t ld, const int32_t* seq_lens,
+                    int32_t B, int32_t max_seq_len, int32_t hq, int32_t hkv, int32_t d,
+                    float sm_scale, int32_t dtype, int32_t num_splits, void* workspace,
+                    size_t ws_bytes, int64_t pool_slots, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RKV_H */

@@ -1,0 +1,385 @@
+// Split-KV single-token decode attention over the token-slot pool.
+//
+// Decoding one token per request (the page's `gen` primitive run step by step;
+// unite.ai, "SGLang: Efficient Execution of Structured Language Model
+// Programs", section "SGLang: Modelo de programacion y metodologia") reads the
+// whole cached K/V of every request once: about 1 flop per byte for plain
+// multi-head attention, 8 for 8-way grouped heads.  The kernel is therefore
+// bound by HBM bandwidth and is built to keep many 16-byte gathers in flight:
+//
+//   phase 1  one workgroup (4 waves) per (split, request, kv head [, head
+//            group]).  A row of K (or V) for one kv head is D elements =
+//            LPR lanes x 16 bytes, so one wave instruction gathers RPW = 64/LPR
+//            whole rows from arbitrary slots, and every wave keeps U rows of K
+//            and U rows of V per lane in flight.  Scores are reduced across the
+//            LPR lanes of a row with DPP row operations; each row group keeps
+//            an fp32 online-softmax state (m, l, acc) per query head; groups
+//            are merged with cross-lane exchanges and then across waves in LDS.
+//            A request whose keys fit in one split writes o and lse directly;
+//            otherwise the split's (m, l, acc) goes to the workspace.
+//   phase 2  one wave per (request, q head) merges the S_r partials by
+//            log-sum-exp rescaling.
+//
+// S_r depends only on L_r (and the caller's num_splits), never on the rest of
+// the batch, so a request's output bits do not depend on its batch.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "device.h"
+#include "rkv.h"
+#include "rkv_internal.h"
+
+namespace {
+
+constexpr int kChunk = 512;     // keys per split under the default rule
+constexpr int kWaves = 4;
+constexpr int kMaxG = 8;        // query heads handled per workgroup
+
+struct DecodeArgs {
+  const void* q;
+  const void* kp;
+  const void* vp;
+  void* o;
+  float* lse;
+  const int32_t* r2t;
+  int64_t ld;
+  const int32_t* seq_lens;
+  int32_t B, hq, hkv, G, hg;      // hg = head groups of <= kMaxG per kv head
+  int32_t splits;                 // grid extent over splits
+  int32_t num_splits;             // 0 = fixed chunk rule
+  float scale_log2e;              // sm_scale * log2(e)
+  int64_t pool_slots;
+  float* ws;                      // [B, hq, splits, D + 2]
+  int* err;
+};
+
+__host__ __device__ inline int split_chunk(int L, int num_splits) {
+  if (num_splits <= 0) return kChunk;
+  int c = (L + num_splits - 1) / num_splits;
+  return ((c + 63) / 64) * 64;
+}
+
+template <typename T>
+struct Elem;
+template <>
+struct Elem<float> {
+  static constexpr int kVec = 4;
+  __device__ static void unpack(const uint4& w, float* f) {
+    f[0] = __builtin_bit_cast(float, w.x);
+    f[1] = __builtin_bit_cast(float, w.y);
+    f[2] = __builtin_bit_cast(float, w.z);
+    f[3] = __builtin_bit_cast(float, w.w);
+  }
+  __device__ static float load1(const void* p, int64_t i) { return ((const float*)p)[i]; }
+  __device__ static void store1(void* p, int64_t i, float v) { ((float*)p)[i] = v; }
+};
+template <>
+struct Elem<uint16_t> {
+  static constexpr int kVec = 8;
+  __device__ static void unpack(const uint4& w, float* f) {
+    f[0] = rkv::bf16lo(w.x); f[1] = rkv::bf16hi(w.x);
+    f[2] = rkv::bf16lo(w.y); f[3] = rkv::bf16hi(w.y);
+    f[4] = rkv::bf16lo(w.z); f[5] = rkv::bf16hi(w.z);
+    f[6] = rkv::bf16lo(w.w); f[7] = rkv::bf16hi(w.w);
+  }
+  __device__ static float load1(const void* p, int64_t i) { return rkv::bf16_to_f32(((const uint16_t*)p)[i]); }
+  __device__ static void store1(void* p, int64_t i, float v) { ((uint16_t*)p)[i] = rkv::f32_to_bf16(v); }
+};
+
+// Combine state b into state a (log2-domain maxima).
+__device__ __forceinline__ void merge_state(float& m, float& l, float* acc, float mb, float lb,
+                                            const float* accb, int n) {
+  const float M = fmaxf(m, mb);
+  if (M == -INFINITY) return;
+  const float fa = exp2f(m - M), fb = exp2f(mb - M);
+  l = l * fa + lb * fb;
+  for (int e = 0; e < n; ++e) acc[e] = acc[e] * fa + accb[e] * fb;
+  m = M;
+}
+
+template <typename T, int D, int G, int U>
+__global__ __launch_bounds__(256) void decode_partial(DecodeArgs a) {
+  using E = Elem<T>;
+  constexpr int VEC = E::kVec;
+  constexpr int LPR = D / VEC;          // lanes per row
+  constexpr int RPW = 64 / LPR;         // rows per wave instruction
+  static_assert(LPR >= 8 && LPR <= 32, "row width");
+
+  const int64_t grid = gridDim.x;
+  const int64_t w = rkv::xcd_work_item(blockIdx.x, grid);
+  const int s = (int)(w % a.splits);
+  int64_t rest = w / a.splits;
+  const int r = (int)(rest % a.B);
+  rest /= a.B;
+  const int sub = (int)(rest % a.hg);
+  const int g = (int)(rest / a.hg);
+  if (g >= a.hkv) return;
+  const int L = a.seq_lens[r];
+  const int chunk = split_chunk(L, a.num_splits);
+  const int nsplit = (L + chunk - 1) / chunk;
+  if (s >= nsplit) return;
+  const int k_begin = s * chunk;
+  const int k_end = min(L, k_begin + chunk);
+  const int h0 = sub * kMaxG;                  // first head of this group within the kv group
+  const int nh = min(G, a.G - h0);              // heads handled here (<= G)
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int lr = lane % LPR;                    // lane within row
+  const int rw = lane / LPR;                    // row within wave instruction
+
+  // queries, pre-scaled into the log2 domain
+  float qv[G][VEC];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const int hh = min(h, nh - 1);
+    const int64_t qoff = ((int64_t)r * a.hq + (int64_t)g * a.G + h0 + hh) * D + lr * VEC;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) qv[h][e] = E::load1(a.q, qoff + e) * a.scale_log2e;
+  }
+  float m[G], l[G], acc[G][VEC];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[h][e] = 0.f;
+  }
+
+  const int32_t* row_tab = a.r2t + (int64_t)r * a.ld;
+  const uint4* kp = (const uint4*)a.kp;
+  const uint4* vp = (const uint4*)a.vp;
+  const int64_t slot_stride = (int64_t)a.hkv * LPR;   // uint4 per slot
+  const int64_t head_off = (int64_t)g * LPR + lr;
+  constexpr int STEP = kWaves * RPW * U;             // keys per workgroup iteration
+
+  for (int base = k_begin; base < k_end; base += STEP) {
+    uint4 kr[U], vr[U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int key = base + (wave * U + u) * RPW + rw;
+      ok[u] = key < k_end;
+      int32_t slot = ok[u] ? row_tab[key] : 0;
+      if (slot < 0 || (int64_t)slot >= a.pool_slots) {
+        if (ok[u]) rkv::raise_flag(a.err);
+        ok[u] = false;
+        slot = 0;
+      }
+      const int64_t off = (int64_t)slot * slot_stride + head_off;
+      kr[u] = ok[u] ? kp[off] : make_uint4(0, 0, 0, 0);
+      vr[u] = ok[u] ? vp[off] : make_uint4(0, 0, 0, 0);
+    }
+    float sc[U][G];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float kf[VEC];
+      E::unpack(kr[u], kf);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float t = 0.f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) t = fmaf(qv[h][e], kf[e], t);
+        sc[u][h] = rkv::group_sum<LPR>(t);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (!ok[u]) sc[u][h] = -INFINITY;
+        mx = fmaxf(mx, sc[u][h]);
+      }
+      const float mn = fmaxf(m[h], mx);
+      const float mref = (mn == -INFINITY) ? 0.f : mn;
+      const float alpha = exp2f(m[h] - mref);
+      l[h] *= alpha;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[h][e] *= alpha;
+      m[h] = mn;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float p = exp2f(sc[u][h] - mref);
+        l[h] += p;
+        float vf[VEC];
+        E::unpack(vr[u], vf);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
+      }
+    }
+  }
+
+  // merge the RPW row groups of this wave (lanes lr, lr+LPR, ...)
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mb = __shfl_xor(m[h], off);
+      const float lb = __shfl_xor(l[h], off);
+      float ab[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) ab[e] = __shfl_xor(acc[h][e], off);
+      merge_state(m[h], l[h], acc[h], mb, lb, ab, VEC);
+    }
+  }
+
+  // merge the 4 waves in LDS: [wave][head][D + 2]
+  __shared__ float red[kWaves][G][D + 2];
+  if (rw == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) red[wave][h][lr * VEC + e] = acc[h][e];
+      if (lr == 0) {
+        red[wave][h][D] = m[h];
+        red[wave][h][D + 1] = l[h];
+      }
+    }
+  }
+  __syncthreads();
+  if (wave != 0 || rw != 0) return;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+#pragma unroll
+    for (int ww = 1; ww < kWaves; ++ww) {
+      float ab[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) ab[e] = red[ww][h][lr * VEC + e];
+      merge_state(m[h], l[h], acc[h], red[ww][h][D], red[ww][h][D + 1], ab, VEC);
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    if (h >= nh) break;
+    const int head = g * a.G + h0 + h;
+    if (nsplit == 1) {
+      const float inv = 1.f / l[h];
+      const int64_t ooff = ((int64_t)r * a.hq + head) * D + lr * VEC;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) E::store1(a.o, ooff + e, acc[h][e] * inv);
+      if (a.lse && lr == 0) a.lse[(int64_t)r * a.hq + head] = (m[h] + log2f(l[h])) * 0.69314718055994531f;
+    } else {
+      float* dst = a.ws + (((int64_t)r * a.hq + head) * a.splits + s) * (D + 2);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) dst[lr * VEC + e] = acc[h][e];
+      if (lr == 0) {
+        dst[D] = m[h];
+        dst[D + 1] = l[h];
+      }
+    }
+  }
+}
+
+// Phase 2: one wave per (request, q head); lanes cover D.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void decode_merge(DecodeArgs a) {
+  using E = Elem<T>;
+  const int64_t w = blockIdx.x;
+  const int r = (int)(w / a.hq);
+  const int head = (int)(w % a.hq);
+  const int L = a.seq_lens[r];
+  const int chunk = split_chunk(L, a.num_splits);
+  const int nsplit = (L + chunk - 1) / chunk;
+  if (nsplit <= 1) return;
+  const int lane = threadIdx.x;
+  const float* src = a.ws + ((int64_t)r * a.hq + head) * a.splits * (D + 2);
+  float M = -INFINITY;
+  for (int s = lane; s < nsplit; s += 64) M = fmaxf(M, src[(int64_t)s * (D + 2) + D]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  constexpr int PER = D / 64;
+  float acc[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+  float lsum = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float* p = src + (int64_t)s * (D + 2);
+    const float ms = p[D];
+    const float f = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
+    lsum += p[D + 1] * f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) acc[i] += p[lane + 64 * i] * f;
+  }
+  const float inv = 1.f / lsum;
+  const int64_t ooff = ((int64_t)r * a.hq + head) * D;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) E::store1(a.o, ooff + lane + 64 * i, acc[i] * inv);
+  if (a.lse && lane == 0) a.lse[(int64_t)r * a.hq + head] = (M + log2f(lsum)) * 0.69314718055994531f;
+}
+
+template <typename T, int D, int G>
+void launch_partial(const DecodeArgs& a, int64_t grid, hipStream_t st) {
+  constexpr int U = (G >= 8) ? 2 : (G >= 4 ? 4 : 8);
+  hipLaunchKernelGGL((decode_partial<T, D, G, U>), dim3((unsigned)grid), dim3(256), 0, st, a);
+}
+
+template <typename T, int D>
+void launch_all(const DecodeArgs& a, int64_t grid, hipStream_t st) {
+  const int g = a.G < kMaxG ? a.G : kMaxG;
+  if (g <= 1) launch_partial<T, D, 1>(a, grid, st);
+  else if (g <= 2) launch_partial<T, D, 2>(a, grid, st);
+  else if (g <= 4) launch_partial<T, D, 4>(a, grid, st);
+  else launch_partial<T, D, 8>(a, grid, st);
+  hipLaunchKernelGGL((decode_merge<T, D>), dim3((unsigned)((int64_t)a.B * a.hq)), dim3(64), 0, st, a);
+}
+
+int64_t splits_extent(int32_t max_seq_len, int32_t num_splits) {
+  if (num_splits > 0) return num_splits;
+  return ((int64_t)max_seq_len + kChunk - 1) / kChunk;
+}
+
+}  // namespace
+
+extern "C" size_t rkv_attn_decode_workspace_bytes(int32_t B, int32_t hq, int32_t d, int32_t max_seq_len,
+                                                  int32_t num_splits) {
+  if (B < 0 || hq < 1 || (d != 64 && d != 128) || max_seq_len < 1 || num_splits < 0) return 0;
+  const int64_t S = splits_extent(max_seq_len, num_splits);
+  return (size_t)B * hq * S * (d + 2) * sizeof(float);
+}
+
+extern "C" int rkv_attn_decode(const void* q, const void* k_pool, const void* v_pool, void* o, float* lse,
+                               const int32_t* req_to_token, int64_t ld, const int32_t* seq_lens,
+                               int32_t B, int32_t max_seq_len, int32_t hq, int32_t hkv, int32_t d,
+                               float sm_scale, int32_t dtype, int32_t num_splits, void* workspace,
+                               size_t ws_bytes, int64_t pool_slots, void* stream) {
+  rkv::clear_error();
+  if (B < 0 || hq < 1 || hkv < 1 || max_seq_len < 1 || ld < max_seq_len || pool_slots < 1 ||
+      num_splits < 0 || !(sm_scale > 0.f))
+    return rkv::fail(RKV_EINVAL, "rkv_attn_decode: bad sizes");
+  if (dtype != RKV_F32 && dtype != RKV_BF16) return rkv::fail(RKV_ENOTSUP, "rkv_attn_decode: dtype");
+  if (d != 64 && d != 128) return rkv::fail(RKV_ENOTSUP, "rkv_attn_decode: head_dim must be 64 or 128");
+  if (hq % hkv != 0 || hq / hkv > 16) return rkv::fail(RKV_ENOTSUP, "rkv_attn_decode: Hq/Hkv must be an integer <= 16");
+  if (B == 0) return RKV_OK;
+  if (!q || !k_pool || !v_pool || !o || !req_to_token || !seq_lens)
+    return rkv::fail(RKV_EINVAL, "rkv_attn_decode: NULL pointer");
+  const uintptr_t al = (uintptr_t)q | (uintptr_t)k_pool | (uintptr_t)v_pool | (uintptr_t)o;
+  if (al & 15) return rkv::fail(RKV_EINVAL, "rkv_attn_decode: tensors must be 16-byte aligned");
+  const size_t need = rkv_attn_decode_workspace_bytes(B, hq, d, max_seq_len, num_splits);
+  const int64_t S = splits_extent(max_seq_len, num_splits);
+  if (S > 1 && (!workspace || ws_bytes < need || ((uintptr_t)workspace & 15)))
+    return rkv::fail(RKV_EINVAL, "rkv_attn_decode: workspace missing or too small");
+  DecodeArgs a;
+  a.q = q; a.kp = k_pool; a.vp = v_pool; a.o = o; a.lse = lse;
+  a.r2t = req_to_token; a.ld = ld; a.seq_lens = seq_lens;
+  a.B = B; a.hq = hq; a.hkv = hkv; a.G = hq / hkv;
+  a.hg = (a.G + kMaxG - 1) / kMaxG;
+  a.splits = (int32_t)S;
+  a.num_splits = num_splits;
+  a.scale_log2e = sm_scale * 1.4426950408889634f;
+  a.pool_slots = pool_slots;
+  a.ws = (float*)workspace;
+  if (int rc = rkv::debug_flag(&a.err)) return rc;
+  int64_t grid = (int64_t)S * B * hkv * a.hg;
+  grid = (grid + rkv::kXcds - 1) / rkv::kXcds * rkv::kXcds;
+  if (grid > 0x7fffffff) return rkv::fail(RKV_ENOTSUP, "rkv_attn_decode: grid too large");
+  hipStream_t st = (hipStream_t)stream;
+  if (dtype == RKV_BF16) {
+    if (d == 128) launch_all<uint16_t, 128>(a, grid, st); else launch_all<uint16_t, 64>(a, grid, st);
+  } else {
+    if (d == 128) launch_all<float, 128>(a, grid, st); else launch_all<float, 64>(a, grid, st);
+  }
+  return rkv::finish_launch("rkv_attn_decode", st, a.err);
+}

@@ -1,0 +1,313 @@
+"""ctypes binding of librkv (include/rkv.h).  Argument marshalling only: every
+step of the path runs in the native library.
+
+Names follow the C ABI without the `rkv_` prefix.  Device entry points take
+torch tensors (torch provides device memory and the current HIP stream) and
+pass their raw pointers; host tree calls take Python sequences or NumPy
+arrays.  Errors raise RkvError carrying the status code and the library's
+message.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librkv.so")
+
+OK, EINVAL, ENOSPC, EBUSY, EHIP, ENOTSUP = 0, -1, -2, -3, -4, -5
+F32, BF16 = 0, 1
+_NAMES = {EINVAL: "EINVAL", ENOSPC: "ENOSPC", EBUSY: "EBUSY", EHIP: "EHIP", ENOTSUP: "ENOTSUP"}
+
+# every symbol include/rkv.h declares
+EXPORTS = (
+    "rkv_last_error", "rkv_version", "rkv_tree_create", "rkv_tree_destroy", "rkv_radix_match",
+    "rkv_radix_lock", "rkv_radix_unlock", "rkv_radix_insert", "rkv_radix_evict", "rkv_alloc",
+    "rkv_free", "rkv_stats", "rkv_radix_serialize", "rkv_free_list", "rkv_batch_prepare",
+    "rkv_batch_commit", "rkv_kv_scatter", "rkv_attn_extend", "rkv_attn_decode_workspace_bytes",
+    "rkv_attn_decode",
+)
+
+
+class RkvError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"{_NAMES.get(code, code)}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+c_i32p = ctypes.POINTER(ctypes.c_int32)
+c_i64p = ctypes.POINTER(ctypes.c_int64)
+_vp = ctypes.c_void_p
+_i32, _i64, _f32, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+
+
+def lib():
+    """Loads librkv.so; raises (never falls back) when it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m prefix_shared_kv_host_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    sig = {
+        "rkv_last_error": (ctypes.c_char_p, []),
+        "rkv_version": (ctypes.c_char_p, []),
+        "rkv_tree_create": (ctypes.c_int, [ctypes.POINTER(_vp), _i64, c_i32p]),
+        "rkv_tree_destroy": (None, [_vp]),
+        "rkv_radix_match": (ctypes.c_int, [_vp, c_i32p, _i64, c_i32p, c_i64p, c_i64p]),
+        "rkv_radix_lock": (ctypes.c_int, [_vp, _i64]),
+        "rkv_radix_unlock": (ctypes.c_int, [_vp, _i64]),
+        "rkv_radix_insert": (ctypes.c_int, [_vp, c_i32p, c_i32p, _i64, c_i64p]),
+        "rkv_radix_evict": (ctypes.c_int, [_vp, _i64, c_i64p]),
+        "rkv_alloc": (ctypes.c_int, [_vp, _i64, c_i32p]),
+        "rkv_free": (ctypes.c_int, [_vp, c_i32p, _i64]),
+        "rkv_stats": (ctypes.c_int, [_vp, c_i64p]),
+        "rkv_radix_serialize": (ctypes.c_int, [_vp, c_i64p, _i64, c_i64p]),
+        "rkv_free_list": (ctypes.c_int, [_vp, c_i32p, _i64, c_i64p]),
+        "rkv_batch_prepare": (ctypes.c_int, [_vp, _i32, c_i32p, c_i64p, c_i32p, _i64, c_i32p, c_i32p,
+                                             c_i32p, c_i32p, _i64, c_i64p]),
+        "rkv_batch_commit": (ctypes.c_int, [_vp, _i32, c_i32p, c_i64p, c_i32p, _i64, c_i64p]),
+        "rkv_kv_scatter": (ctypes.c_int, [_vp, _vp, _vp, _i64, _vp, _vp, _i64, _i32, _i32, _i32, _vp]),
+        "rkv_attn_extend": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _i32, _i64, _i32,
+                                           _i32, _i32, _i32, _f32, _i32, _i64, _vp]),
+        "rkv_attn_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+        "rkv_attn_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32, _i32, _i32, _i32,
+                                           _i32, _f32, _i32, _i32, _vp, _sz, _i64, _vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(code):
+    if code != OK:
+        raise RkvError(code, lib().rkv_last_error().decode())
+    return code
+
+
+def version() -> str:
+    return lib().rkv_version().decode()
+
+
+def _i32arr(x):
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+    return a, a.ctypes.data_as(c_i32p)
+
+
+class Tree:
+    """Radix tree + FIFO slot allocator (host).  Methods mirror rkv_radix_*,
+    rkv_alloc/free, rkv_batch_*; status codes other than OK raise RkvError
+    unless the method documents returning them."""
+
+    def __init__(self, pool_slots: int, initial_free=None):
+        self._h = _vp()
+        self.pool_slots = int(pool_slots)
+        if initial_free is None:
+            _check(lib().rkv_tree_create(ctypes.byref(self._h), self.pool_slots, None))
+        else:
+            a, p = _i32arr(initial_free)
+            if a.shape[0] != self.pool_slots:
+                raise RkvError(EINVAL, "initial_free must have pool_slots entries")
+            _check(lib().rkv_tree_create(ctypes.byref(self._h), self.pool_slots, p))
+
+    def close(self):
+        if self._h:
+            lib().rkv_tree_destroy(self._h)
+            self._h = _vp()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- single operations -------------------------------------------------
+    def radix_match(self, tok):
+        a, p = _i32arr(tok)
+        out = np.empty(max(1, a.shape[0]), dtype=np.int32)
+        m, node = _i64(), _i64()
+        _check(lib().rkv_radix_match(self._h, p, a.shape[0], out.ctypes.data_as(c_i32p),
+                                     ctypes.byref(m), ctypes.byref(node)))
+        return m.value, out[: m.value].tolist(), node.value
+
+    def radix_lock(self, node) -> int:
+        return lib().rkv_radix_lock(self._h, int(node))
+
+    def radix_unlock(self, node) -> int:
+        return lib().rkv_radix_unlock(self._h, int(node))
+
+    def radix_insert(self, tok, slots) -> int:
+        a, p = _i32arr(tok)
+        b, q = _i32arr(slots)
+        if a.shape[0] != b.shape[0]:
+            return EINVAL
+        out = _i64()
+        code = lib().rkv_radix_insert(self._h, p, q, a.shape[0], ctypes.byref(out))
+        return out.value if code == OK else code
+
+    def radix_evict(self, want):
+        """Returns (status, freed); EBUSY is returned, not raised."""
+        out = _i64()
+        code = lib().rkv_radix_evict(self._h, int(want), ctypes.byref(out))
+        if code not in (OK, EBUSY):
+            _check(code)
+        return code, out.value
+
+    def alloc(self, n):
+        """Returns (status, slots); ENOSPC is returned, not raised."""
+        out = np.empty(max(1, int(n)), dtype=np.int32)
+        code = lib().rkv_alloc(self._h, int(n), out.ctypes.data_as(c_i32p))
+        if code not in (OK, ENOSPC):
+            _check(code)
+        return code, (out[: int(n)].tolist() if code == OK else [])
+
+    def free(self, slots) -> int:
+        a, p = _i32arr(slots)
+        return lib().rkv_free(self._h, p, a.shape[0])
+
+    def stats(self):
+        out = np.zeros(8, dtype=np.int64)
+        _check(lib().rkv_stats(self._h, out.ctypes.data_as(c_i64p)))
+        return out.tolist()
+
+    def radix_serialize(self):
+        n = _i64()
+        _check(lib().rkv_radix_serialize(self._h, None, 0, ctypes.byref(n)))
+        buf = np.empty(n.value, dtype=np.int64)
+        _check(lib().rkv_radix_serialize(self._h, buf.ctypes.data_as(c_i64p), n.value, ctypes.byref(n)))
+        return buf.tolist()
+
+    def free_list(self):
+        n = _i64()
+        _check(lib().rkv_free_list(self._h, None, 0, ctypes.byref(n)))
+        buf = np.empty(max(1, n.value), dtype=np.int32)
+        _check(lib().rkv_free_list(self._h, buf.ctypes.data_as(c_i32p), n.value, ctypes.byref(n)))
+        return buf[: n.value].tolist()
+
+    # -- batches ------------------------------------------------------------
+    @staticmethod
+    def _flat(seqs):
+        lens = np.array([len(s) for s in seqs], dtype=np.int64)
+        indptr = np.zeros(len(seqs) + 1, dtype=np.int64)
+        np.cumsum(lens, out=indptr[1:])
+        flat = (np.concatenate([np.asarray(s, dtype=np.int32) for s in seqs])
+                if len(seqs) else np.zeros(0, dtype=np.int32))
+        return np.ascontiguousarray(flat, dtype=np.int32), indptr, lens
+
+    def batch_prepare(self, seqs, ld=None):
+        """Returns (status, tables); tables hold NumPy arrays req_to_token
+        [B, ld], prefix_lens, seq_lens, qo_indptr [B+1], new_slots [T] and
+        nodes.  EBUSY is returned, not raised."""
+        B = len(seqs)
+        flat, indptr, lens = self._flat(seqs)
+        if ld is None:
+            ld = int(lens.max()) if B else 1
+        r2t = np.empty((max(B, 1), ld), dtype=np.int32)
+        pl = np.empty(max(B, 1), dtype=np.int32)
+        sl = np.empty(max(B, 1), dtype=np.int32)
+        qo = np.zeros(B + 1, dtype=np.int32)
+        cap = int(lens.sum())
+        ns = np.empty(max(cap, 1), dtype=np.int32)
+        nodes = np.empty(max(B, 1), dtype=np.int64)
+        code = lib().rkv_batch_prepare(
+            self._h, B, flat.ctypes.data_as(c_i32p), indptr.ctypes.data_as(c_i64p),
+            r2t.ctypes.data_as(c_i32p), int(ld), pl.ctypes.data_as(c_i32p), sl.ctypes.data_as(c_i32p),
+            qo.ctypes.data_as(c_i32p), ns.ctypes.data_as(c_i32p), cap, nodes.ctypes.data_as(c_i64p))
+        if code == EBUSY:
+            return code, None
+        _check(code)
+        T = int(qo[B])
+        return OK, dict(req_to_token=r2t[:B], prefix_lens=pl[:B], seq_lens=sl[:B], qo_indptr=qo,
+                        new_slots=ns[:T], nodes=nodes[:B], ld=int(ld))
+
+    def batch_commit(self, seqs, req_to_token, nodes) -> int:
+        B = len(seqs)
+        flat, indptr, _ = self._flat(seqs)
+        r2t = np.ascontiguousarray(np.asarray(req_to_token, dtype=np.int32))
+        nd = np.ascontiguousarray(np.asarray(nodes, dtype=np.int64))
+        ld = r2t.shape[1] if r2t.ndim == 2 and B else 1
+        return _check(lib().rkv_batch_commit(self._h, B, flat.ctypes.data_as(c_i32p),
+                                             indptr.ctypes.data_as(c_i64p), r2t.ctypes.data_as(c_i32p),
+                                             int(ld), nd.ctypes.data_as(c_i64p)))
+
+
+# ---------------------------------------------------------------------------
+# device entry points (torch tensors in, pointers out)
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise RkvError(ENOTSUP, f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise RkvError(EINVAL, "device entry points take GPU tensors")
+        if t is not None and not t.is_contiguous():
+            raise RkvError(EINVAL, "tensors must be contiguous")
+
+
+def kv_scatter(k_new, v_new, slots, k_pool, v_pool, stream=None):
+    """k_pool[slots[i]] = k_new[i]; v_pool[slots[i]] = v_new[i]."""
+    _need_cuda(k_new, v_new, slots, k_pool, v_pool)
+    P, hkv, d = k_pool.shape
+    return _check(lib().rkv_kv_scatter(_ptr(k_new), _ptr(v_new), _ptr(slots), int(slots.shape[0]),
+                                       _ptr(k_pool), _ptr(v_pool), int(P), int(hkv), int(d),
+                                       _dtype_code(k_pool), _stream(stream)))
+
+
+def attn_extend(q, k_pool, v_pool, o, req_to_token, qo_indptr, prefix_lens, max_new, lse=None,
+                sm_scale=None, stream=None):
+    """Causal extend attention of q [T, Hq, D] over each request's cached
+    prefix plus its new tokens; writes o (and lse when given)."""
+    _need_cuda(q, k_pool, v_pool, o, req_to_token, qo_indptr, prefix_lens, lse)
+    T, hq, d = q.shape
+    P, hkv, _ = k_pool.shape
+    B = int(prefix_lens.shape[0])
+    scale = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
+    return _check(lib().rkv_attn_extend(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(o), _ptr(lse), _ptr(req_to_token),
+        int(req_to_token.shape[1]), _ptr(qo_indptr), _ptr(prefix_lens), B, int(T), int(max_new),
+        int(hq), int(hkv), int(d), scale, _dtype_code(q), int(P), _stream(stream)))
+
+
+def attn_decode_workspace_bytes(B, hq, d, max_seq_len, num_splits=0) -> int:
+    return int(lib().rkv_attn_decode_workspace_bytes(int(B), int(hq), int(d), int(max_seq_len),
+                                                     int(num_splits)))
+
+
+def attn_decode(q, k_pool, v_pool, o, req_to_token, seq_lens, max_seq_len, workspace, lse=None,
+                num_splits=0, sm_scale=None, stream=None):
+    """Single-token split-KV decode of q [B, Hq, D] over all seq_lens[r] keys."""
+    _need_cuda(q, k_pool, v_pool, o, req_to_token, seq_lens, lse, workspace)
+    B, hq, d = q.shape
+    P, hkv, _ = k_pool.shape
+    scale = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return _check(lib().rkv_attn_decode(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(o), _ptr(lse), _ptr(req_to_token),
+        int(req_to_token.shape[1]), _ptr(seq_lens), int(B), int(max_seq_len), int(hq), int(hkv),
+        int(d), scale, _dtype_code(q), int(num_splits), _ptr(workspace), int(ws_bytes), int(P),
+        _stream(stream)))

@@ -1,0 +1,58 @@
+"""Native radix tree + allocator vs the oracle, bit-exact: op-for-op on
+seeded random streams (outputs, free-list order and canonical dumps after
+every op), the walkthrough, and whole workload traces through
+batch_prepare / batch_commit.  CPU only (host code of librkv)."""
+import numpy as np
+import pytest
+
+from inputs import configs
+from oracle.radix import OracleTree
+from tests import radix_ops, walkthrough
+from tests.native_tree import NativeTree
+
+
+@pytest.mark.parametrize("seed,vocab", [(1, 2), (2, 3), (3, 4), (4, 2), (5, 3)])
+def test_native_matches_oracle_op_by_op(seed, vocab):
+    P = 48
+    perm = np.random.default_rng(100 + seed).permutation(P).tolist()
+    c = radix_ops.drive([OracleTree(P, perm), NativeTree(P, perm)], seed, 20000, P, vocab, 12)
+    assert c["split"] > 50 and c["evicted_nodes"] > 200
+
+
+def test_native_walkthrough():
+    walkthrough.run(lambda P: NativeTree(P))
+
+
+def _replay(name, limit=None):
+    shape, phases = configs.build(name)
+    perm = configs.free_list(shape.pool, shape.seed)
+    trees = [OracleTree(shape.pool, perm), NativeTree(shape.pool, perm)]
+    for i, ph in enumerate(phases[:limit]):
+        res = [t.batch_prepare(ph.seqs) for t in trees]
+        assert res[0][0] == res[1][0] == 0, (name, i)
+        a, b = res[0][1], res[1][1]
+        for key in ("prefix_lens", "seq_lens", "qo_indptr", "new_slots", "nodes"):
+            assert list(a[key]) == list(b[key]), (name, i, key)
+        for r in range(len(ph.seqs)):
+            assert list(a["req_to_token"][r]) == list(b["req_to_token"][r]), (name, i, r)
+        for t, (_, tb) in zip(trees, res):
+            assert t.batch_commit(ph.seqs, tb["req_to_token"], tb["nodes"]) == 0
+        assert trees[0].stats() == trees[1].stats(), (name, i)
+        assert trees[0].free_list() == trees[1].free_list(), (name, i)
+    assert trees[0].serialize() == trees[1].serialize()
+    return trees[0]
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c3ns", "c4"])
+def test_workload_tables_bit_exact(name):
+    _replay(name)
+
+
+@pytest.mark.parametrize("name", ["c5", "c5e"])
+def test_chat_trace_tables_bit_exact(name):
+    t = _replay(name)
+    s = t.stats()
+    if name == "c5e":
+        assert s[7] > 100000      # the 2^19 pool really evicts
+    else:
+        assert s[7] == 0          # the 2^21 pool never binds
