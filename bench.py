@@ -1,0 +1,311 @@
+"""Benchmark: RadixAttention prefix-shared KV attention on one MI355X.
+
+One step = one pass of the device hot path over the two Llama-7B-shaped
+batches (32 q / 32 kv heads, head_dim 128, bf16):
+
+  extend  64 requests share a cached 1024-token prefix and extend 128 new
+          tokens each: kv_scatter of the 8192 new tokens' K/V, then
+          attn_extend (bf16 MFMA);
+  decode  256 requests under a 4-ary, depth-3 radix tree with private tails
+          (contexts 512..4096), one new token each: kv_scatter, then the
+          split-KV attn_decode.
+
+Index tables come from the native radix tree (batch_prepare, untimed) and are
+resident in HBM when the timed region starts.  value = tokens per second of
+the whole step (8192 + 256 tokens).  Extend TFLOP/s and decode KV GB/s are
+reported against the MI355X peaks (2516.6 TFLOP/s dense bf16, 8 TB/s HBM),
+per kernel from HIP events on the launch stream.  The host radix operations
+are timed separately (ns per token).  The float64 oracle is timed on a
+bounded sample on the host cores (rank 0 only).
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "extend attn TFLOP/s + decode KV GB/s (frac of peak); tokens/s, 1 MI355X"
+PEAK_BF16_TFLOPS = 2516.6
+PEAK_HBM_GBS = 8000.0
+
+
+def extend_flops(prefix_lens, seq_lens, hq, d):
+    p = np.asarray(prefix_lens, dtype=np.float64)
+    n = np.asarray(seq_lens, dtype=np.float64) - p
+    return float(4.0 * d * hq * np.sum(n * p + n * (n + 1) / 2))
+
+
+def decode_bytes(seq_lens, hq, hkv, d, b, unique_slots=None):
+    L = np.asarray(seq_lens, dtype=np.float64)
+    B = L.shape[0]
+    kv_tokens = L.sum() if unique_slots is None else float(unique_slots)
+    return float(kv_tokens * hkv * d * 2 * b + 4 * L.sum() + 2 * B * hq * d * b)
+
+
+def scatter_bytes(T, hkv, d, b):
+    return float(4 * T * hkv * d * b + 4 * T)
+
+
+class Phase:
+    """A prepared batch whose tables and new-token K/V/Q sit in HBM."""
+
+    def __init__(self, name, cfg_fn, kind_index):
+        import torch
+        from inputs import configs, content
+        from prefix_shared_kv_host_amd.engine import RadixKVCache
+
+        self.shape, phases = cfg_fn()
+        s = self.shape
+        dt = content.torch_dtype(s.dtype)
+        perm = configs.free_list(s.pool, s.seed)
+        self.cache = RadixKVCache(s.pool, s.hkv, s.d, dt, "cuda", perm)
+        self.radix_ns = []
+        for i, ph in enumerate(phases):
+            t0 = time.perf_counter()
+            batch = self.cache.prepare(ph.seqs)
+            t1 = time.perf_counter()
+            q, k, v = content.batch_rows(s.seed, ph.seqs, batch.host["prefix_lens"], s.hq, s.hkv, s.d,
+                                         dt, "cuda", s.q_scale, with_q=(i == kind_index))
+            self.cache.store(batch, k, v)
+            if i == kind_index:
+                self.batch, self.q, self.k, self.v = batch, q, k, v
+                self.kind = ph.kind
+                self.prepare_s = t1 - t0
+                self.tokens_in_batch = int(batch.host["seq_lens"].sum())
+                break
+            t2 = time.perf_counter()
+            self.cache.commit(batch)
+            self.radix_ns.append((t1 - t0 + time.perf_counter() - t2) * 1e9 / max(1, sum(map(len, ph.seqs))))
+        torch.cuda.synchronize()
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty(self.q.shape[0], s.hq, dtype=torch.float32, device="cuda")
+        if self.kind == "decode":
+            B, hq, _ = self.q.shape
+            self.cache.workspace(B, hq, self.batch.max_len)
+        self.name = name
+
+    def scatter(self):
+        self.cache.store(self.batch, self.k, self.v)
+
+    def attend(self):
+        if self.kind == "extend":
+            self.cache.extend(self.batch, self.q, self.o, self.lse)
+        else:
+            self.cache.decode(self.batch, self.q, self.o, self.lse)
+
+
+def time_host_radix(phase_obj, reps=3):
+    """ns per token of batch_prepare + batch_commit on a fresh native tree
+    replaying the same workload (host only)."""
+    from inputs import configs
+    from prefix_shared_kv_host_amd import rkv
+    s, phases = phase_obj.cfg
+    best = None
+    for _ in range(reps):
+        t = rkv.Tree(s.pool, configs.free_list(s.pool, s.seed))
+        tot_tok, tot_s = 0, 0.0
+        for ph in phases:
+            t0 = time.perf_counter()
+            code, tb = t.batch_prepare(ph.seqs)
+            t.batch_commit(ph.seqs, tb["req_to_token"], tb["nodes"])
+            tot_s += time.perf_counter() - t0
+            tot_tok += sum(map(len, ph.seqs))
+        v = tot_s * 1e9 / tot_tok
+        best = v if best is None else min(best, v)
+    return best
+
+
+def cpu_baseline(budget_s=20.0):
+    """The float64 oracle on a bounded sample of the same two batches."""
+    import torch
+    from inputs import configs, content
+    from oracle import attention as oatt
+    from oracle.pool import OraclePool, scatter
+    from oracle.radix import OracleTree
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        blas = os.cpu_count()
+
+    def sample_run(cfg_fn, kind, keep):
+        s, phases = cfg_fn()
+        tree = OracleTree(s.pool, configs.free_list(s.pool, s.seed))
+        pool = OraclePool(s.pool, s.hkv, s.d)
+        dt = content.torch_dtype(s.dtype)
+        for ph in phases:
+            if ph.kind == kind:
+                seqs = [ph.seqs[r] for r in keep]
+                # the sampled requests' cached parts, then the batch itself
+                st, tb = tree.batch_prepare(seqs)
+                q, k, v = content.batch_rows(s.seed, seqs, [0] * len(seqs), s.hq, s.hkv, s.d, dt, "cpu",
+                                             s.q_scale, with_q=False)
+                # content for every position of the sampled sequences (prefix
+                # rows are a pure function of the prefix, so this equals the
+                # cached rows)
+                slots = []
+                for r in range(len(seqs)):
+                    slots += tb["req_to_token"][r][: tb["seq_lens"][r]]
+                scatter(pool, slots, k, v)
+                qq, _, _ = content.batch_rows(s.seed, seqs, tb["prefix_lens"], s.hq, s.hkv, s.d, dt, "cpu",
+                                              s.q_scale, with_q=True)
+                qn = qq.float().numpy()
+                t0 = time.perf_counter()
+                if kind == "extend":
+                    oatt.extend(qn, pool, tb["req_to_token"], tb["qo_indptr"], tb["prefix_lens"], s.hq, s.hkv)
+                else:
+                    oatt.decode(qn, pool, tb["req_to_token"], tb["seq_lens"], s.hq, s.hkv)
+                dt_s = time.perf_counter() - t0
+                return dt_s, int(tb["qo_indptr"][-1])
+            st, tb = tree.batch_prepare(ph.seqs)
+            tree.batch_commit(ph.seqs, tb["req_to_token"], tb["nodes"])
+        raise RuntimeError("no such phase")
+
+    te, ne = sample_run(configs.c2, "extend", list(range(0, 64, 4)))      # 16 of 64 requests
+    td, nd = sample_run(configs.c3, "decode", list(range(0, 256, 4)))     # 64 of 256 requests
+    # scale to one full step: 64 extend requests + 256 decode requests
+    t_step = te * 64 / 16 + td * 256 / 64
+    return dict(value=(8192 + 256) / t_step, unit="tokens/s", cores=int(blas), kind="oracle",
+                sample="float64 oracle attention on 16 of the 64 extend requests (all 32 heads) and 64 "
+                       "of the 256 decode requests, scaled to one full step",
+                seconds=te + td, extend_s_sample=te, decode_s_sample=td)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-reps", type=int, default=10)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this path has no sharding or collectives "
+              "(see DESIGN.md for how it would shard).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from inputs import configs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    t_setup = time.perf_counter()
+    ext = Phase("extend", configs.c2, 1)
+    ext.cfg = configs.c2()
+    dec = Phase("decode", configs.c3, 4)
+    dec.cfg = configs.c3()
+    print(f"# setup {time.perf_counter() - t_setup:.1f}s", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+
+    def step(record=False):
+        if record:
+            ev[0].record(stream)
+        ext.scatter()
+        if record:
+            ev[1].record(stream)
+        ext.attend()
+        if record:
+            ev[2].record(stream)
+        dec.scatter()
+        if record:
+            ev[3].record(stream)
+        dec.attend()
+        if record:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, synchronized on both sides
+    per = np.zeros((args.steps, 4))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(record=True)
+        torch.cuda.synchronize()
+        per[i] = [ev[j].elapsed_time(ev[j + 1]) for j in range(4)]
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1000 / args.steps
+    ms_kernels = per.sum(axis=1).mean()
+    kern_ms = per.mean(axis=0)   # scatter_e, extend, scatter_d, decode
+
+    # cold: flush L2 / MALL with a 512 MiB write before each launch
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    cold = np.zeros((args.cold_reps, 2))
+    for i in range(args.cold_reps):
+        flush.fill_(i & 0xFF)
+        ev[0].record(stream); ext.attend(); ev[1].record(stream)
+        flush.fill_((i + 1) & 0xFF)
+        ev[2].record(stream); dec.attend(); ev[3].record(stream)
+        torch.cuda.synchronize()
+        cold[i] = [ev[0].elapsed_time(ev[1]), ev[2].elapsed_time(ev[3])]
+    del flush
+
+    s_e, s_d = ext.shape, dec.shape
+    tb_e, tb_d = ext.batch.host, dec.batch.host
+    F = extend_flops(tb_e["prefix_lens"], tb_e["seq_lens"], s_e.hq, s_e.d)
+    uniq = len(np.unique(np.concatenate([tb_d["req_to_token"][r][: tb_d["seq_lens"][r]]
+                                         for r in range(len(tb_d["seq_lens"]))])))
+    Bl = decode_bytes(tb_d["seq_lens"], s_d.hq, s_d.hkv, s_d.d, 2)
+    Bu = decode_bytes(tb_d["seq_lens"], s_d.hq, s_d.hkv, s_d.d, 2, unique_slots=uniq)
+    T_e, T_d = int(tb_e["qo_indptr"][-1]), int(tb_d["qo_indptr"][-1])
+    ext_tflops = F / (kern_ms[1] * 1e-3) / 1e12
+    dec_gbs = Bl / (kern_ms[3] * 1e-3) / 1e9
+    dec_gbs_u = Bu / (kern_ms[3] * 1e-3) / 1e9
+    tokens = T_e + T_d
+    value = tokens / (ms_per_step * 1e-3)
+
+    extend_obj = dict(kernel="attn_extend (bf16 MFMA)", us=kern_ms[1] * 1e3, us_cold=cold[:, 0].mean() * 1e3,
+                      flop=F, tflops=ext_tflops, frac_of_peak=ext_tflops / PEAK_BF16_TFLOPS,
+                      tokens_per_s=T_e / ((kern_ms[0] + kern_ms[1]) * 1e-3), scatter_us=kern_ms[0] * 1e3,
+                      scatter_gbs=scatter_bytes(T_e, s_e.hkv, s_e.d, 2) / (kern_ms[0] * 1e-3) / 1e9,
+                      hit_rate=float(np.sum(tb_e["prefix_lens"]) / np.sum(tb_e["seq_lens"])))
+    decode_obj = dict(kernel="attn_decode (split-KV partial + LSE merge)", us=kern_ms[3] * 1e3,
+                      us_cold=cold[:, 1].mean() * 1e3, bytes_logical=Bl, bytes_unique=Bu,
+                      gbs_logical=dec_gbs, gbs_unique=dec_gbs_u, frac_of_peak=dec_gbs / PEAK_HBM_GBS,
+                      frac_of_peak_unique=dec_gbs_u / PEAK_HBM_GBS,
+                      tokens_per_s=T_d / ((kern_ms[2] + kern_ms[3]) * 1e-3), scatter_us=kern_ms[2] * 1e3)
+    roof_e = dict(kernel="attn_extend", bound="mfma", achieved=ext_tflops, peak=PEAK_BF16_TFLOPS,
+                  unit="TFLOP/s", frac=ext_tflops / PEAK_BF16_TFLOPS, traffic=None)
+    roof_d = dict(kernel="attn_decode", bound="hbm", achieved=dec_gbs, peak=PEAK_HBM_GBS, unit="GB/s",
+                  frac=dec_gbs / PEAK_HBM_GBS, traffic=None)
+    dominant_is_decode = kern_ms[3] >= kern_ms[1]
+    out = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "llama7b-fewshot-extend (64 req x (1024 shared + 128 new), 32/32 heads, "
+                               "D=128, 2^20 slots) + llama7b-radix-decode (256 req, 4-ary depth-3 tree, "
+                               "ctx 512-4096)",
+                   "global_batch": 64 + 256, "tokens_per_step": tokens, "parallelism": "single-gpu"},
+        "extend": extend_obj, "decode": decode_obj,
+        "roofline": roof_d if dominant_is_decode else roof_e,
+        "roofline_other": roof_e if dominant_is_decode else roof_d,
+        "ms_kernels_per_step": ms_kernels,
+        "host_radix_ns_per_token": {"extend_workload": time_host_radix(ext),
+                                    "decode_workload": time_host_radix(dec)},
+        "context": "the pages' up-to-6.4x end-to-end throughput was measured on NVIDIA A10G/A100 "
+                   "against other serving systems; it is not comparable to this number",
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

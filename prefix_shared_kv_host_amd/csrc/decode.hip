@@ -47,6 +47,7 @@ struct DecodeArgs {
   int64_t ld;
   const int32_t* seq_lens;
   int32_t B, hq, hkv, G, hg;      // hg = head groups of <= kMaxG per kv head
+  int32_t max_seq_len;            // every length is clamped to it (<= ld)
   int32_t splits;                 // grid extent over splits
   int32_t num_splits;             // 0 = fixed chunk rule
   float scale_log2e;              // sm_scale * log2(e)
@@ -116,7 +117,7 @@ __global__ __launch_bounds__(256) void decode_partial(DecodeArgs a) {
   const int sub = (int)(rest % a.hg);
   const int g = (int)(rest / a.hg);
   if (g >= a.hkv) return;
-  const int L = a.seq_lens[r];
+  const int L = min(a.seq_lens[r], a.max_seq_len);
   const int chunk = split_chunk(L, a.num_splits);
   const int nsplit = (L + chunk - 1) / chunk;
   if (s >= nsplit) return;
@@ -280,7 +281,7 @@ __global__ __launch_bounds__(64) void decode_merge(DecodeArgs a) {
   const int64_t w = blockIdx.x;
   const int r = (int)(w / a.hq);
   const int head = (int)(w % a.hq);
-  const int L = a.seq_lens[r];
+  const int L = min(a.seq_lens[r], a.max_seq_len);
   const int chunk = split_chunk(L, a.num_splits);
   const int nsplit = (L + chunk - 1) / chunk;
   if (nsplit <= 1) return;
@@ -366,6 +367,7 @@ extern "C" int rkv_attn_decode(const void* q, const void* k_pool, const void* v_
   a.r2t = req_to_token; a.ld = ld; a.seq_lens = seq_lens;
   a.B = B; a.hq = hq; a.hkv = hkv; a.G = hq / hkv;
   a.hg = (a.G + kMaxG - 1) / kMaxG;
+  a.max_seq_len = max_seq_len;
   a.splits = (int32_t)S;
   a.num_splits = num_splits;
   a.scale_log2e = sm_scale * 1.4426950408889634f;

@@ -59,6 +59,7 @@ struct ExtendArgs {
   float scale_log2e;
   int64_t pool_slots;
   int64_t tiles_bound;      // work items per kv head
+  int64_t total_new;        // q rows; rows at or past it are never read
   int* err;
 };
 
@@ -139,7 +140,8 @@ __global__ __launch_bounds__(256, 2) void extend_bf16(ExtendArgs a) {
   const int rows_total = n * G;
   const int row0 = t * BM;
   const int row_last = min(row0 + BM, rows_total) - 1;
-  const int kv_end = p + row_last / G + 1;
+  // keys never reach past the table row, whatever the lengths say
+  const int kv_end = (int)min((int64_t)p + row_last / G + 1, a.ld);
   const int ntiles = (kv_end + BN - 1) / BN;
 
   // ---- queries of this wave: rows row0 + wave*32 + qb*16 + l16
@@ -150,7 +152,7 @@ __global__ __launch_bounds__(256, 2) void extend_bf16(ExtendArgs a) {
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int row = row0 + wave * 32 + qb * 16 + l16;
-    qvalid[qb] = row < rows_total;
+    qvalid[qb] = row < rows_total && (int64_t)q0 + row / G < a.total_new && p + row / G < kv_end;
     const int j = qvalid[qb] ? row / G : 0;
     const int hh = qvalid[qb] ? row % G : 0;
     qtok[qb] = q0 + j;
@@ -372,7 +374,7 @@ __global__ __launch_bounds__(256) void extend_f32(ExtendArgs a) {
   }
   const int r = lo;
   const int j = (int)(row - a.qo_indptr[r]);
-  const int c = a.prefix_lens[r] + j;
+  const int c = (int)min((int64_t)a.prefix_lens[r] + j, a.ld - 1);
   const int g = head / a.G;
   const float* qf = (const float*)a.q + (row * a.hq + head) * D;
   float qv[PER], acc[PER];
@@ -436,6 +438,7 @@ extern "C" int rkv_attn_extend(const void* q, const void* k_pool, const void* v_
   a.B = B; a.hq = hq; a.hkv = hkv; a.G = hq / hkv;
   a.scale_log2e = sm_scale * 1.4426950408889634f;
   a.pool_slots = pool_slots;
+  a.total_new = total_new;
   if (int rc = rkv::debug_flag(&a.err)) return rc;
   hipStream_t st = (hipStream_t)stream;
   if (dtype == RKV_BF16) {

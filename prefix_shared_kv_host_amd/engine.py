@@ -1,0 +1,98 @@
+"""RadixKVCache: one token-slot KV pool on a GPU plus its radix tree.
+
+A thin orchestration of the C-ABI calls in the order RadixAttention serves a
+batch (unite.ai, "SGLang: Efficient Execution of Structured Language Model
+Programs", walkthrough in section "SGLang: Modelo de programacion y
+metodologia"): prepare (match the cached prefixes, lock them, allocate slots
+for the rest, evicting least-recently-used nodes if the pool is short), store
+the new tokens' K/V, attend, commit (insert the sequences, unlock).  Every
+step runs in librkv; this module only moves arguments and owns the device
+buffers (torch supplies the memory and the stream).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import rkv
+
+POISON = {torch.bfloat16: 0x7FC0, torch.float32: 0x7FC00000}
+
+
+@dataclass
+class Batch:
+    seqs: list
+    host: dict                  # NumPy tables from batch_prepare
+    req_to_token: torch.Tensor  # device int32 [B, ld]
+    qo_indptr: torch.Tensor
+    prefix_lens: torch.Tensor
+    seq_lens: torch.Tensor
+    new_slots: torch.Tensor
+    max_new: int
+    max_len: int
+    total_new: int
+
+
+class RadixKVCache:
+    def __init__(self, pool_slots: int, hkv: int, d: int, dtype=torch.bfloat16, device="cuda",
+                 initial_free=None, poison: bool = True):
+        self.pool_slots, self.hkv, self.d, self.dtype = int(pool_slots), hkv, d, dtype
+        self.device = torch.device(device)
+        self.tree = rkv.Tree(pool_slots, initial_free)
+        shape = (self.pool_slots, hkv, d)
+        if poison:
+            bits = torch.int16 if dtype == torch.bfloat16 else torch.int32
+            val = POISON[dtype]
+            val = val - (1 << 16) if (bits == torch.int16 and val >= 1 << 15) else val
+            self.k_pool = torch.full(shape, val, dtype=bits, device=self.device).view(dtype)
+            self.v_pool = torch.full(shape, val, dtype=bits, device=self.device).view(dtype)
+        else:
+            self.k_pool = torch.empty(shape, dtype=dtype, device=self.device)
+            self.v_pool = torch.empty(shape, dtype=dtype, device=self.device)
+        self._ws = None
+
+    # ---------------------------------------------------------------- host
+    def prepare(self, seqs, ld=None) -> Batch:
+        code, tb = self.tree.batch_prepare(seqs, ld)
+        if code != rkv.OK:
+            raise rkv.RkvError(code, "batch_prepare: eviction cannot free enough slots")
+
+        def up(a):
+            return torch.from_numpy(np.ascontiguousarray(a)).pin_memory().to(self.device, non_blocking=True)
+
+        n = tb["seq_lens"].astype(np.int64) - tb["prefix_lens"]
+        return Batch(seqs=seqs, host=tb, req_to_token=up(tb["req_to_token"]), qo_indptr=up(tb["qo_indptr"]),
+                     prefix_lens=up(tb["prefix_lens"]), seq_lens=up(tb["seq_lens"]),
+                     new_slots=up(tb["new_slots"]), max_new=int(n.max()) if len(n) else 0,
+                     max_len=int(tb["seq_lens"].max()) if len(n) else 0, total_new=int(tb["qo_indptr"][-1]))
+
+    def commit(self, batch: Batch):
+        self.tree.batch_commit(batch.seqs, batch.host["req_to_token"], batch.host["nodes"])
+
+    # ---------------------------------------------------------------- device
+    def store(self, batch: Batch, k_new, v_new, stream=None):
+        rkv.kv_scatter(k_new, v_new, batch.new_slots, self.k_pool, self.v_pool, stream)
+
+    def extend(self, batch: Batch, q, o=None, lse=None, stream=None):
+        if o is None:
+            o = torch.empty_like(q)
+        rkv.attn_extend(q, self.k_pool, self.v_pool, o, batch.req_to_token, batch.qo_indptr,
+                        batch.prefix_lens, batch.max_new, lse=lse, stream=stream)
+        return o
+
+    def workspace(self, B, hq, max_len, num_splits=0):
+        need = rkv.attn_decode_workspace_bytes(B, hq, self.d, max_len, num_splits)
+        if self._ws is None or self._ws.numel() * 4 < need:
+            self._ws = torch.empty(max(need // 4, 1), dtype=torch.float32, device=self.device)
+        return self._ws
+
+    def decode(self, batch: Batch, q, o=None, lse=None, num_splits=0, stream=None):
+        if o is None:
+            o = torch.empty_like(q)
+        B, hq, _ = q.shape
+        ws = self.workspace(B, hq, batch.max_len, num_splits)
+        rkv.attn_decode(q, self.k_pool, self.v_pool, o, batch.req_to_token, batch.seq_lens,
+                        batch.max_len, ws, lse=lse, num_splits=num_splits, stream=stream)
+        return o

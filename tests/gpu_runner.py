@@ -1,0 +1,147 @@
+"""Runs a workload through the native path on the GPU and through the oracle
+on the CPU, side by side.
+
+Both sides get the same seeded input rows (from `inputs.content`) and nothing
+else: the oracle builds its own tree, tables and pool (and the tables are
+asserted bit-exact against the library's), and computes attention in float64.
+"""
+from __future__ import annotations
+
+import math
+import sys
+import time
+
+import numpy as np
+import torch
+
+from inputs import configs, content
+from oracle import attention as oatt
+from oracle.pool import OraclePool, scatter as oscatter
+from oracle.radix import OracleTree
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+LSE_TOL = {"f32": 1e-5, "bf16": 1e-4}
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def needed_slots(shape, phases, select):
+    """Dry run of the oracle tree: slots the selected requests will read."""
+    t = OracleTree(shape.pool, configs.free_list(shape.pool, shape.seed))
+    need = set()
+    for i, ph in enumerate(phases):
+        st, tb = t.batch_prepare(ph.seqs)
+        assert st == 0
+        reqs = select(i, len(ph.seqs)) if ph.kind in ("extend", "decode") else []
+        if reqs is None:
+            reqs = range(len(ph.seqs))
+        for r in reqs:
+            need.update(tb["req_to_token"][r][: tb["seq_lens"][r]])
+        t.batch_commit(ph.seqs, tb["req_to_token"], tb["nodes"])
+    return need
+
+
+def run(shape, phases, select=lambda i, B: None, num_splits=0, content_device="cuda",
+        with_lse=True, sparse=False):
+    """Returns a list of per-checked-phase dicts with GPU and oracle outputs
+    restricted to the selected requests' rows."""
+    from prefix_shared_kv_host_amd.engine import RadixKVCache
+
+    dt = content.torch_dtype(shape.dtype)
+    perm = configs.free_list(shape.pool, shape.seed)
+    otree = OracleTree(shape.pool, perm)
+    opool = OraclePool(shape.pool, shape.hkv, shape.d)
+    cache = RadixKVCache(shape.pool, shape.hkv, shape.d, dt, "cuda", perm)
+    keep = None
+    if sparse:
+        keep = np.zeros(shape.pool, dtype=bool)
+        keep[list(needed_slots(shape, phases, select))] = True
+    out = []
+    for i, ph in enumerate(phases):
+        t0 = time.time()
+        st, otb = otree.batch_prepare(ph.seqs)
+        assert st == 0
+        batch = cache.prepare(ph.seqs)
+        for key in ("prefix_lens", "seq_lens", "qo_indptr", "new_slots"):
+            assert list(otb[key]) == batch.host[key].tolist(), (shape.name, i, key)
+        for r in range(len(ph.seqs)):
+            L = otb["seq_lens"][r]
+            assert list(otb["req_to_token"][r][:L]) == batch.host["req_to_token"][r][:L].tolist()
+        reqs = select(i, len(ph.seqs)) if ph.kind in ("extend", "decode") else []
+        attend = reqs is None or len(reqs) > 0
+        q, k, v = content.batch_rows(shape.seed, ph.seqs, otb["prefix_lens"], shape.hq, shape.hkv,
+                                     shape.d, dt, content_device, shape.q_scale, with_q=attend)
+        cache.store(batch, k.to("cuda"), v.to("cuda"))
+        slots = np.asarray(otb["new_slots"], dtype=np.int64)
+        if keep is not None:
+            sel = np.nonzero(keep[slots])[0]
+            idx = torch.from_numpy(sel).to(k.device)
+            oscatter(opool, slots[sel], k.index_select(0, idx).cpu(), v.index_select(0, idx).cpu())
+        else:
+            oscatter(opool, slots, k.cpu(), v.cpu())
+        if attend:
+            qd = q.to("cuda")
+            rows = qd.shape[0]
+            lse = torch.full((rows, shape.hq), float("nan"), device="cuda") if with_lse else None
+            if ph.kind == "extend":
+                o = cache.extend(batch, qd, lse=lse)
+            else:
+                o = cache.decode(batch, qd, lse=lse, num_splits=num_splits)
+            torch.cuda.synchronize()
+            B = len(ph.seqs)
+            rq = list(range(B)) if reqs is None else list(reqs)
+            qn = q.float().cpu().numpy()
+            if ph.kind == "extend":
+                o_ref, lse_ref = oatt.extend(qn, opool, otb["req_to_token"], otb["qo_indptr"],
+                                             otb["prefix_lens"], shape.hq, shape.hkv, requests=rq)
+                row_idx = np.concatenate([np.arange(otb["qo_indptr"][r], otb["qo_indptr"][r + 1]) for r in rq])
+            else:
+                o_ref, lse_ref = oatt.decode(qn, opool, otb["req_to_token"], otb["seq_lens"],
+                                             shape.hq, shape.hkv, requests=rq)
+                row_idx = np.array(rq, dtype=np.int64)
+            og = o.float().cpu().numpy()[row_idx]
+            lg = lse.cpu().numpy()[row_idx] if with_lse else None
+            out.append(dict(phase=i, kind=ph.kind, requests=rq, o=og, o_ref=o_ref[row_idx], lse=lg,
+                            lse_ref=lse_ref[row_idx], o_full=o, batch=batch))
+            log(f"[{shape.name}] phase {i} {ph.kind} B={B} checked={len(rq)} "
+                f"({time.time() - t0:.1f}s)")
+        otree.batch_commit(ph.seqs, otb["req_to_token"], otb["nodes"])
+        cache.commit(batch)
+    return out, cache
+
+
+def check(res, dtype, name=""):
+    """Asserts the tolerance on every compared element; returns a report."""
+    rep = []
+    for r in res:
+        err = np.abs(r["o"] - r["o_ref"])
+        nan = int(np.isnan(r["o"]).sum())
+        mx = float(np.nanmax(err)) if err.size else 0.0
+        rel = mx / max(float(np.abs(r["o_ref"]).max()), 1e-30)
+        line = dict(phase=r["phase"], max_abs=mx, rel=rel, mean_abs=float(err.mean()), nan=nan)
+        if r["lse"] is not None:
+            line["lse_max_abs"] = float(np.abs(r["lse"] - r["lse_ref"]).max())
+        log(f"  {name} {line}")
+        rep.append(line)
+        assert nan == 0, (name, line)
+        assert mx <= TOL[dtype], (name, line)
+        if r["lse"] is not None:
+            assert line["lse_max_abs"] <= LSE_TOL[dtype], (name, line)
+    return rep
+
+
+def sample(seed, k):
+    """Seeded selector: k requests per checked phase (all when B <= k)."""
+    def f(i, B):
+        if B <= k:
+            return None
+        rng = np.random.default_rng(seed * 1000 + i)
+        return sorted(rng.choice(B, size=k, replace=False).tolist())
+    return f
+
+
+def sm_scale(d):
+    return 1.0 / math.sqrt(d)

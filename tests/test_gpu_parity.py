@@ -1,0 +1,135 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle on
+the same seeded inputs.  bf16: max-abs <= 2e-2; fp32: max-abs <= 1e-5; lse
+<= 1e-4 / 1e-5; no NaN (unused pool slots hold NaN poison, so a wrong gather
+shows up)."""
+import numpy as np
+import pytest
+import torch
+
+from inputs import configs
+from tests import gpu_runner as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from prefix_shared_kv_host_amd import rkv
+    rkv.lib()   # fail loudly if the native library is missing
+    G.log(f"device: {torch.cuda.get_device_name(0)}")
+
+
+# ---------------------------------------------------------------- scatter
+@pytest.mark.parametrize("dtype,hkv,d", [(torch.bfloat16, 4, 128), (torch.float32, 2, 64),
+                                         (torch.bfloat16, 8, 64)])
+def test_kv_scatter_bit_exact(dtype, hkv, d):
+    from prefix_shared_kv_host_amd.engine import RadixKVCache
+    from prefix_shared_kv_host_amd import rkv
+    P, T = 1000, 333
+    cache = RadixKVCache(P, hkv, d, dtype, "cuda")
+    before_k = cache.k_pool.clone()
+    g = torch.Generator().manual_seed(3)
+    slots = torch.randperm(P, generator=g)[:T].to(torch.int32)
+    k = torch.randn(T, hkv, d, generator=g).to(dtype)
+    v = torch.randn(T, hkv, d, generator=g).to(dtype)
+    rkv.kv_scatter(k.cuda(), v.cuda(), slots.cuda(), cache.k_pool, cache.v_pool)
+    torch.cuda.synchronize()
+    bits = torch.int16 if dtype == torch.bfloat16 else torch.int32
+    kp, vp = cache.k_pool.cpu().view(bits), cache.v_pool.cpu().view(bits)
+    s = slots.long()
+    assert torch.equal(kp[s], k.view(bits)) and torch.equal(vp[s], v.view(bits))
+    rest = torch.ones(P, dtype=torch.bool)
+    rest[s] = False
+    assert torch.equal(kp[rest], before_k.cpu().view(bits)[rest])
+    assert torch.equal(vp[rest], before_k.cpu().view(bits)[rest])   # both pools start as poison
+
+
+# ---------------------------------------------------------------- extend
+TINY = [
+    # dtype, hq, hkv, d
+    ("f32", 4, 4, 64), ("f32", 4, 2, 128), ("bf16", 4, 4, 128), ("bf16", 8, 2, 128),
+    ("bf16", 4, 4, 64), ("bf16", 16, 2, 64), ("bf16", 12, 4, 128),
+]
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d", TINY)
+def test_extend_tiny_ragged(dtype, hq, hkv, d):
+    shape, phases = configs.tiny(41, hq=hq, hkv=hkv, d=d, dtype=dtype, pool=4096, prefix=70,
+                                 new=(1, 37, 64, 3, 129))
+    res, _ = G.run(shape, phases, content_device="cpu")
+    G.check(res, dtype, f"tiny {dtype} {hq}/{hkv} d{d}")
+
+
+def test_extend_c1_fp32():
+    shape, phases = configs.c1()
+    res, _ = G.run(shape, phases, content_device="cpu")
+    G.check(res, "f32", "c1")
+
+
+@pytest.mark.parametrize("name", ["c2", "c2s"])
+def test_extend_c2_every_row(name):
+    shape, phases = configs.build(name)
+    res, _ = G.run(shape, phases)
+    rep = G.check(res, "bf16", name)
+    if name == "c2s":
+        assert np.abs(res[0]["o_ref"]).max() > 0.5      # peaked weights: |o| ~ 1
+
+
+@pytest.mark.timeout(400)
+def test_extend_c4_subset():
+    shape, phases = configs.c4()
+    sel = lambda i, B: ([0, 5, 17, 22, 31, 40, 53, 63] if phases[i].kind == "extend" else [])
+    res, _ = G.run(shape, phases[:3], select=sel, sparse=True)
+    G.check(res, "bf16", "c4-extend")
+
+
+# ---------------------------------------------------------------- decode
+def decode_workload(shape, lengths, shared=300, seed=7):
+    """Histories cached in a setup batch, then one decode batch whose
+    requests add one token each.  Half the requests share a prefix."""
+    rng = np.random.default_rng(seed)
+    pre = [int(x) for x in rng.integers(0, 32000, shared)]
+    full = []
+    for i, L in enumerate(lengths):
+        if i % 2 == 0 and L > shared + 1:
+            tail = [int(x) for x in rng.integers(0, 32000, L - shared)]
+            tail[0] = 40000 + i          # distinct branch after the shared prefix
+            full.append(pre + tail)
+        else:
+            seq = [int(x) for x in rng.integers(0, 32000, L)]
+            seq[0] = 50000 + i           # distinct first token
+            full.append(seq)
+    hist = [f[:-1] for f in full if len(f) > 1]
+    return [configs.Phase("setup", hist), configs.Phase("decode", full)]
+
+
+DEC_LENS = [1, 2, 63, 64, 65, 511, 512, 513, 1100, 1201, 300, 302]
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d,splits", [
+    ("bf16", 4, 4, 128, 0), ("bf16", 8, 1, 128, 3), ("f32", 4, 2, 64, 0), ("bf16", 16, 2, 64, 5),
+    ("f32", 2, 2, 128, 7), ("bf16", 6, 2, 128, 2),
+])
+def test_decode_tiny_ragged(dtype, hq, hkv, d, splits):
+    shape = configs.Shape(f"dec-{dtype}-{hq}-{hkv}-{d}", hq, hkv, d, dtype, 8192, 43)
+    phases = decode_workload(shape, DEC_LENS)
+    res, _ = G.run(shape, phases, num_splits=splits, content_device="cpu")
+    assert res[0]["batch"].host["qo_indptr"].tolist() == list(range(len(DEC_LENS) + 1))
+    G.check(res, dtype, f"decode {dtype} {hq}/{hkv} d{d} s{splits}")
+
+
+@pytest.mark.timeout(400)
+@pytest.mark.parametrize("name", ["c3", "c3ns"])
+def test_decode_c3_sampled(name):
+    shape, phases = configs.build(name)
+    res, _ = G.run(shape, phases, select=G.sample(3, 24), sparse=True)
+    G.check(res, "bf16", name)
+
+
+@pytest.mark.timeout(400)
+def test_decode_c4_sampled():
+    shape, phases = configs.c4()
+    ph = [phases[0], phases[1], phases[3]]
+    res, _ = G.run(shape, ph, select=G.sample(4, 16), sparse=True)
+    G.check(res, "bf16", "c4-decode")
