@@ -203,6 +203,8 @@ int rkv_kv_scatter(const void* k_new, const void* v_new, const int32_t* slots, i
  * of the longer requests unwritten).  The new tokens' K/V must already be in the pool (rkv_kv_scatter).
  * bf16: QK^T and PV on bf16 MFMA with fp32 accumulation, fp32 online
  * softmax, softmax weights rounded to bf16 for PV, o rounded to bf16 (RNE).
+ * The row sums that normalize o (and give lse) are sums of those same
+ * rounded weights, so bf16 lse is within ln(1 + 2^-8) of the exact value.
  * f32: fp32 arithmetic throughout.  B = 0 or total_new = 0 is a no-op. */
 int rkv_attn_extend(const void* q, const void* k_pool, const void* v_pool, void* o, float* lse,
                     const int32_t* req_to_token, int64_t ld, const int32_t* qo_indptr,

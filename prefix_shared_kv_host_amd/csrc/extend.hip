@@ -33,6 +33,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "device.h"
 #include "rkv.h"
 #include "rkv_internal.h"
@@ -106,6 +108,12 @@ __device__ __forceinline__ int key_of_row(int rho) {
   return c * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
 }
 
+// Softmax weights are kept relative to a per-row reference maximum that is
+// only raised when a tile's maximum exceeds it by more than 2^8 (log2 units):
+// weights stay <= 256, harmless in fp32 and bf16, and the O accumulators are
+// rescaled only on those rare tiles instead of on every tile.
+constexpr float kRescaleThreshold = 8.0f;
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void extend_bf16(ExtendArgs a) {
   constexpr int KP = D + 8;          // K row pitch in LDS (elements)
@@ -118,8 +126,12 @@ __global__ __launch_bounds__(256, 2) void extend_bf16(ExtendArgs a) {
   constexpr int KPT = BN * CPR / 256;  // V keys per thread (transposed group)
   static_assert(KPT == 2 || KPT == 4, "V transpose group");
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
+  // two stages: the next tile is written while the current one is read;
+  // slot indices run one more tile ahead in three small stages, so a K/V
+  // gather never waits on a global index load
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VP];
+  __shared__ __attribute__((aligned(16))) int32_t Sl[3][BN];
 
   const int64_t w = rkv::xcd_work_item(blockIdx.x, gridDim.x);
   const int g = (int)(w / a.tiles_bound);
@@ -130,7 +142,7 @@ __global__ __launch_bounds__(256, 2) void extend_bf16(ExtendArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15;
   const int gq = lane >> 4;
   const int q0 = a.qo_indptr[r];
@@ -143,10 +155,12 @@ __global__ __launch_bounds__(256, 2) void extend_bf16(ExtendArgs a) {
   // keys never reach past the table row, whatever the lengths say
   const int kv_end = (int)min((int64_t)p + row_last / G + 1, a.ld);
   const int ntiles = (kv_end + BN - 1) / BN;
+  // tiles before this one are fully visible to every row of the workgroup
+  const int first_mask_tile = min(ntiles, (p + row0 / G) / BN);
 
   // ---- queries of this wave: rows row0 + wave*32 + qb*16 + l16
   bf16x8 qreg[2][KSTEPS];
-  int qpos[2], qhead[2], qtok[2];
+  int qlim[2], qhead[2], qtok[2];
   bool qvalid[2];
   const uint16_t* qbase = (const uint16_t*)a.q;
 #pragma unroll
@@ -157,7 +171,8 @@ __global__ __launch_bounds__(256, 2) void extend_bf16(ExtendArgs a) {
     const int hh = qvalid[qb] ? row % G : 0;
     qtok[qb] = q0 + j;
     qhead[qb] = g * G + hh;
-    qpos[qb] = qvalid[qb] ? p + j : kv_end - 1;
+    // last visible key, relative to the first key this lane holds in a tile
+    qlim[qb] = (qvalid[qb] ? p + j : kv_end - 1) - 8 * gq;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
       uint4 v = make_uint4(0, 0, 0, 0);
@@ -166,62 +181,61 @@ __global__ __launch_bounds__(256, 2) void extend_bf16(ExtendArgs a) {
       qreg[qb][s] = __builtin_bit_cast(bf16x8, v);
     }
   }
-  const int wave_row0 = row0 + wave * 32;
-  const int wave_qmin = p + min(wave_row0, rows_total - 1) / G;
 
   f32x4 oacc[2][DBLK];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) oacc[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float mrow[2] = {-INFINITY, -INFINITY};
-  float lrow[2] = {0.f, 0.f};
+  float mref[2] = {-INFINITY, -INFINITY};
+  // row sums of the bf16 weights, accumulated on the MFMA (all-ones A
+  // operand) so that numerator and denominator use the same rounded weights;
+  // every element of lacc[qb] holds the lane's full row sum
+  f32x4 lacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+  const float c = a.scale_log2e;
 
-  // ---- tile loader assignments
+  // ---- tile loader: every gathered row index is clamped into [0, kv_end)
+  //      and every slot into [0, pool_slots), so no access leaves the table or
+  //      the pool; keys past kv_end are masked by the causal test.
   const int32_t* row_tab = a.r2t + (int64_t)r * a.ld;
-  const uint4* kp = (const uint4*)a.kp;
-  const uint4* vp = (const uint4*)a.vp;
-  const int64_t slot_stride = (int64_t)a.hkv * CPR;  // uint4 per slot
-  const int64_t head_off = (int64_t)g * CPR;
+  const char* kp = (const char*)a.kp;
+  const char* vp = (const char*)a.vp;
+  constexpr int ROWB = D * 2;          // bytes of one (slot, kv head) row
   const int kc = tid % CPR;            // K chunk (16 bytes) this thread moves
   const int krow = tid / CPR;          // first K LDS row this thread moves
   const int vdg = tid % CPR;           // V: 8-wide d group
   const int vkq = tid / CPR;           // V: group of KPT keys
+  const uint32_t P = (uint32_t)min(a.pool_slots, (int64_t)0x7fffffff);
 
+  // slot of a key of this request, clamped into the table and the pool
+  auto fetch_slot = [&](int key) -> int32_t {
+    int32_t slot = row_tab[min(key, kv_end - 1)];
+    if ((uint32_t)slot >= P) {
+      if (a.err) rkv::raise_flag(a.err);
+      slot = 0;
+    }
+    return slot;
+  };
+  auto gather = [&](const char* base, int32_t slot, int chunk) -> uint4 {
+    const uint64_t off = ((uint64_t)(uint32_t)slot * (uint32_t)a.hkv + (uint32_t)g) * ROWB + chunk * 16;
+    return *(const uint4*)(base + off);
+  };
   uint4 kreg[KPASS], vreg[KPT];
   auto load_tile = [&](int tile) {
+    const int32_t* sl = Sl[tile % 3];
 #pragma unroll
-    for (int i = 0; i < KPASS; ++i) {
-      const int key = tile * BN + key_of_row(krow + i * KROWS);
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (key < kv_end) {
-        const int32_t slot = row_tab[key];
-        if (slot >= 0 && (int64_t)slot < a.pool_slots)
-          v = kp[(int64_t)slot * slot_stride + head_off + kc];
-        else
-          rkv::raise_flag(a.err);
-      }
-      kreg[i] = v;
-    }
+    for (int i = 0; i < KPASS; ++i) kreg[i] = gather(kp, sl[key_of_row(krow + i * KROWS)], kc);
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int key = tile * BN + vkq * KPT + u;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (key < kv_end) {
-        const int32_t slot = row_tab[key];
-        if (slot >= 0 && (int64_t)slot < a.pool_slots)
-          v = vp[(int64_t)slot * slot_stride + head_off + vdg];
-        else
-          rkv::raise_flag(a.err);
-      }
-      vreg[u] = v;
-    }
+    for (int u = 0; u < KPT; ++u) vreg[u] = gather(vp, sl[vkq * KPT + u], vdg);
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](int buf) {
+    uint16_t* ks = Ks[buf];
+    uint16_t* vt = Vt[buf];
 #pragma unroll
     for (int i = 0; i < KPASS; ++i)
-      *(uint4*)(Ks + (krow + i * KROWS) * KP + kc * 8) = kreg[i];
-    // V transposed: element (d, key) at Vt[d*VP + ((key/8) ^ (d/8 & 7))*8 + key%8]
+      *(uint4*)(ks + (krow + i * KROWS) * KP + kc * 8) = kreg[i];
+    // V transposed: element (d, key) at vt[d*VP + ((key/8) ^ (d/8 & 7))*8 + key%8]
     const int key0 = vkq * KPT;
     const int phys = ((key0 >> 3) ^ (vdg & 7)) * 8 + (key0 & 7);
     const uint32_t* w32[KPT];
@@ -232,28 +246,25 @@ __global__ __launch_bounds__(256, 2) void extend_bf16(ExtendArgs a) {
 #pragma unroll
       for (int hi = 0; hi < 2; ++hi) {
         const int d = vdg * 8 + e2 * 2 + hi;
-        uint32_t pk[KPT / 2];
+        uint32_t pk[2];
 #pragma unroll
         for (int u = 0; u < KPT; u += 2) {
           const uint32_t x0 = w32[u][e2], x1 = w32[u + 1][e2];
-          pk[u / 2] = hi ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
+          pk[u / 2] = hi ? __builtin_amdgcn_perm(x1, x0, 0x07060302u) : __builtin_amdgcn_perm(x1, x0, 0x05040100u);
         }
-        if (KPT == 4)
-          *(uint2*)(Vt + d * VP + phys) = make_uint2(pk[0], pk[KPT / 2 - 1]);
+        if constexpr (KPT == 4)
+          *(uint2*)(vt + d * VP + phys) = make_uint2(pk[0], pk[1]);
         else
-          *(uint32_t*)(Vt + d * VP + phys) = pk[0];
+          *(uint32_t*)(vt + d * VP + phys) = pk[0];
       }
     }
   };
 
-  load_tile(0);
-  for (int tile = 0; tile < ntiles; ++tile) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (tile + 1 < ntiles) load_tile(tile + 1);
-
-    // ---- S^T = K Q^T for 64 keys x 2 query blocks
+  // one 64-key tile: S^T = K Q^T, online softmax, O^T += V^T P^T
+  auto tile_body = [&](int tile, int buf, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const uint16_t* ks = Ks[buf];
+    const uint16_t* vt = Vt[buf];
     f32x4 sacc[2][4];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
@@ -263,84 +274,104 @@ __global__ __launch_bounds__(256, 2) void extend_bf16(ExtendArgs a) {
     for (int s = 0; s < KSTEPS; ++s) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const bf16x8 ka = __builtin_bit_cast(bf16x8, *(const uint4*)(Ks + (kb * 16 + l16) * KP + s * 32 + gq * 8));
+        const bf16x8 ka = __builtin_bit_cast(bf16x8, *(const uint4*)(ks + (kb * 16 + l16) * KP + s * 32 + gq * 8));
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
           sacc[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qreg[qb][s], sacc[qb][kb], 0, 0, 0);
       }
     }
-
-    // ---- online softmax; lane owns query l16 of each block, keys
-    //      tile*64 + c*32 + 8*gq + 4*half + i  for block kb = 2c + half
-    const bool need_mask = tile * BN + BN - 1 > wave_qmin;
+    // lane owns query l16 of each block and keys
+    //   tile*64 + 32*(kb/2) + 8*gq + 4*(kb%2) + i   (block kb, element i)
     bf16x8 pb[2][2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      float mx = -INFINITY;
+      if constexpr (MASK) {
+        const int lim = qlim[qb] - tile * BN;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = sacc[qb][kb][i];
-          if (need_mask) {
-            const int key = tile * BN + (kb >> 1) * 32 + 8 * gq + 4 * (kb & 1) + i;
-            if (key > qpos[qb]) v = -INFINITY;
-          }
-          sacc[qb][kb][i] = v;
-          mx = fmaxf(mx, v);
-        }
+          for (int i = 0; i < 4; ++i)
+            if (32 * (kb >> 1) + 4 * (kb & 1) + i > lim) sacc[qb][kb][i] = -INFINITY;
       }
+      float mx = fmaxf(fmaxf(sacc[qb][0][0], sacc[qb][0][1]), fmaxf(sacc[qb][0][2], sacc[qb][0][3]));
+#pragma unroll
+      for (int kb = 1; kb < 4; ++kb)
+        mx = fmaxf(mx, fmaxf(fmaxf(sacc[qb][kb][0], sacc[qb][kb][1]), fmaxf(sacc[qb][kb][2], sacc[qb][kb][3])));
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(mrow[qb], mx * a.scale_log2e);
-      const float alpha = exp2f(mrow[qb] - mnew);
-      mrow[qb] = mnew;
-      float psum = 0.f;
+      const float mt = mx * c;
+      if (__builtin_amdgcn_ballot_w64(mt > mref[qb] + kRescaleThreshold)) {
+        const float mn = fmaxf(mref[qb], mt);
+        const float alpha = __builtin_amdgcn_exp2f(mref[qb] - mn);
+        mref[qb] = mn;
+        lacc[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) oacc[qb][db] *= alpha;
+      }
+      const float m = mref[qb];
       float pv[4][4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e = exp2f(fmaf(sacc[qb][kb][i], a.scale_log2e, -mnew));
-          pv[kb][i] = e;
-          psum += e;
-        }
-      lrow[qb] = lrow[qb] * alpha + psum;
+        for (int i = 0; i < 4; ++i) pv[kb][i] = __builtin_amdgcn_exp2f(fmaf(sacc[qb][kb][i], c, -m));
 #pragma unroll
-      for (int db = 0; db < DBLK; ++db) oacc[qb][db] *= alpha;
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
+      for (int cc = 0; cc < 2; ++cc) {
         uint4 u;
-        u.x = rkv::pack_bf16x2(pv[2 * c][0], pv[2 * c][1]);
-        u.y = rkv::pack_bf16x2(pv[2 * c][2], pv[2 * c][3]);
-        u.z = rkv::pack_bf16x2(pv[2 * c + 1][0], pv[2 * c + 1][1]);
-        u.w = rkv::pack_bf16x2(pv[2 * c + 1][2], pv[2 * c + 1][3]);
-        pb[qb][c] = __builtin_bit_cast(bf16x8, u);
+        u.x = rkv::pack_bf16x2(pv[2 * cc][0], pv[2 * cc][1]);
+        u.y = rkv::pack_bf16x2(pv[2 * cc][2], pv[2 * cc][3]);
+        u.z = rkv::pack_bf16x2(pv[2 * cc + 1][0], pv[2 * cc + 1][1]);
+        u.w = rkv::pack_bf16x2(pv[2 * cc + 1][2], pv[2 * cc + 1][3]);
+        pb[qb][cc] = __builtin_bit_cast(bf16x8, u);
       }
     }
-
-    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+        lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[qb][cc], lacc[qb], 0, 0, 0);
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) {
       const int d = db * 16 + l16;
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int phys = ((c * 4 + gq) ^ ((d >> 3) & 7)) * 8;
-        const bf16x8 va = __builtin_bit_cast(bf16x8, *(const uint4*)(Vt + d * VP + phys));
+      for (int cc = 0; cc < 2; ++cc) {
+        const int phys = ((cc * 4 + gq) ^ ((d >> 3) & 7)) * 8;
+        const bf16x8 va = __builtin_bit_cast(bf16x8, *(const uint4*)(vt + d * VP + phys));
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
-          oacc[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[qb][c], oacc[qb][db], 0, 0, 0);
+          oacc[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[qb][cc], oacc[qb][db], 0, 0, 0);
       }
     }
+  };
+
+  // prologue: slots of tiles 0 and 1, then tile 0 itself
+  if (tid < BN) Sl[0][tid] = fetch_slot(tid);
+  else if (tid < 2 * BN && ntiles > 1) Sl[1][tid - BN] = fetch_slot(tid);
+  __syncthreads();
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  // iteration t: gather tile t+1 and the slots of tile t+2 while computing
+  // tile t; then publish both and meet at the barrier
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const bool more = tile + 1 < ntiles;
+    const bool more2 = tile + 2 < ntiles;
+    if (more) load_tile(tile + 1);
+    int32_t sreg = 0;
+    if (more2 && tid < BN) sreg = fetch_slot((tile + 2) * BN + tid);
+    if (tile < first_mask_tile)
+      tile_body(tile, tile & 1, std::false_type{});
+    else
+      tile_body(tile, tile & 1, std::true_type{});
+    if (more) store_tile((tile + 1) & 1);
+    if (more2 && tid < BN) Sl[(tile + 2) % 3][tid] = sreg;
+    __syncthreads();
   }
 
   // ---- epilogue: lane holds o[query l16][d = db*16 + 4*gq + 0..3]
   uint16_t* obase = (uint16_t*)a.o;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    float lsum = lrow[qb];
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
+    const float lsum = lacc[qb][0];
     if (!qvalid[qb]) continue;
     const float inv = 1.f / lsum;
     uint16_t* orow = obase + ((int64_t)qtok[qb] * a.hq + qhead[qb]) * D;
@@ -351,7 +382,7 @@ __global__ __launch_bounds__(256, 2) void extend_bf16(ExtendArgs a) {
           make_uint2(rkv::pack_bf16x2(v[0] * inv, v[1] * inv), rkv::pack_bf16x2(v[2] * inv, v[3] * inv));
     }
     if (a.lse && gq == 0)
-      a.lse[(int64_t)qtok[qb] * a.hq + qhead[qb]] = (mrow[qb] + log2f(lsum)) * 0.69314718055994531f;
+      a.lse[(int64_t)qtok[qb] * a.hq + qhead[qb]] = (mref[qb] + log2f(lsum)) * 0.69314718055994531f;
   }
 }
 

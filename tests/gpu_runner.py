@@ -20,7 +20,10 @@ from oracle.pool import OraclePool, scatter as oscatter
 from oracle.radix import OracleTree
 
 TOL = {"f32": 1e-5, "bf16": 2e-2}
-LSE_TOL = {"f32": 1e-5, "bf16": 1e-4}
+# bf16 extend sums the same bf16-rounded weights that PV uses, so its lse
+# carries their rounding: |ln(sum p^) - ln(sum p)| <= ln(1 + 2^-8) < 3.9e-3
+# (unit roundoff of bf16).  fp32 paths and decode keep fp32 weights.
+LSE_TOL = {"f32": 1e-5, "bf16": 3.9e-3}
 
 
 def log(msg):
