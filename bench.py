@@ -254,7 +254,28 @@ def main():
         ev[2].record(stream); dec.attend(); ev[3].record(stream)
         torch.cuda.synchronize()
         cold[i] = [ev[0].elapsed_time(ev[1]), ev[2].elapsed_time(ev[3])]
+    # no-share control: the same context lengths with every context private,
+    # so no KV row is read by two requests (honest HBM fraction for decode)
+    ns = Phase("decode-noshare", configs.c3ns, 1)
+    ns_ms = []
+    for i in range(args.warmup + args.steps):
+        ev[0].record(stream); ns.attend(); ev[1].record(stream)
+        torch.cuda.synchronize()
+        if i >= args.warmup:
+            ns_ms.append(ev[0].elapsed_time(ev[1]))
+    ns_cold = []
+    for i in range(args.cold_reps):
+        flush.fill_(i & 0xFF)
+        ev[0].record(stream); ns.attend(); ev[1].record(stream)
+        torch.cuda.synchronize()
+        ns_cold.append(ev[0].elapsed_time(ev[1]))
     del flush
+    tb_n = ns.batch.host
+    Bn = decode_bytes(tb_n["seq_lens"], ns.shape.hq, ns.shape.hkv, ns.shape.d, 2)
+    ns_us = float(np.mean(ns_ms)) * 1e3
+    noshare_obj = dict(kernel="attn_decode", us=ns_us, us_cold=float(np.mean(ns_cold)) * 1e3, bytes=Bn,
+                       gbs=Bn / (ns_us * 1e-6) / 1e9, frac_of_peak=Bn / (ns_us * 1e-6) / 1e9 / PEAK_HBM_GBS)
+    del ns
 
     s_e, s_d = ext.shape, dec.shape
     tb_e, tb_d = ext.batch.host, dec.batch.host
@@ -293,7 +314,7 @@ def main():
                                "D=128, 2^20 slots) + llama7b-radix-decode (256 req, 4-ary depth-3 tree, "
                                "ctx 512-4096)",
                    "global_batch": 64 + 256, "tokens_per_step": tokens, "parallelism": "single-gpu"},
-        "extend": extend_obj, "decode": decode_obj,
+        "extend": extend_obj, "decode": decode_obj, "decode_noshare_control": noshare_obj,
         "roofline": roof_d if dominant_is_decode else roof_e,
         "roofline_other": roof_e if dominant_is_decode else roof_d,
         "ms_kernels_per_step": ms_kernels,

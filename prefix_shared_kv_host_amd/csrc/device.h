@@ -65,6 +65,20 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Max over lanes l and l^32 (resp. l^16): gfx950 permlane swaps exchange
+// the two 32-lane halves (resp. neighbouring 16-lane rows) in VALU, without
+// an LDS round trip.
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                                  false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                                  false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+
 // Raises the debug error flag (a plain vector store; any writer stores 1).
 __device__ __forceinline__ void raise_flag(int* err) {
   if (err) __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

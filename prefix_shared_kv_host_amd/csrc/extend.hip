@@ -99,6 +99,9 @@ __device__ bool locate_tile(const ExtendArgs& a, int64_t tg, int& r, int& t) {
   return false;
 }
 
+// Physical 16-byte chunk of logical chunk `ch` (8 keys) in V^T row d.
+__device__ __forceinline__ int vt_chunk(int ch, int d) { return ch ^ ((d ^ (d >> 3)) & 7); }
+
 // Key held by K LDS row rho of a 64-key tile.  Within each 32-key chunk,
 // rows 0..15 hold keys 8*(i/4) + i%4 and rows 16..31 hold 8*(i/4) + 4 + i%4,
 // so MFMA block kb = 2c + half gives lane group gq the keys
@@ -116,8 +119,12 @@ constexpr float kRescaleThreshold = 8.0f;
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void extend_bf16(ExtendArgs a) {
-  constexpr int KP = D + 8;          // K row pitch in LDS (elements)
-  constexpr int VP = BN + 8;         // V^T row pitch in LDS (elements)
+  // LDS layouts, chosen with a bank-conflict probe on gfx950: a 16-row
+  // ds_read_b128 pattern is conflict-free when the row pitch is 2 mod 4
+  // 16-byte chunks (K: D + 16 elements), or at a 128-byte pitch when the
+  // chunk index is XOR-swizzled by the row (V^T, see vt_chunk)
+  constexpr int KP = D + 16;         // K row pitch in LDS (elements)
+  constexpr int VP = BN;             // V^T row pitch in LDS (elements)
   constexpr int KSTEPS = D / 32;     // QK contraction steps
   constexpr int DBLK = D / 16;       // PV output blocks
   constexpr int CPR = D / 8;         // 16-byte chunks per K/V row
@@ -204,8 +211,12 @@ __global__ __launch_bounds__(256, 2) void extend_bf16(ExtendArgs a) {
   constexpr int ROWB = D * 2;          // bytes of one (slot, kv head) row
   const int kc = tid % CPR;            // K chunk (16 bytes) this thread moves
   const int krow = tid / CPR;          // first K LDS row this thread moves
-  const int vdg = tid % CPR;           // V: 8-wide d group
-  const int vkq = tid / CPR;           // V: group of KPT keys
+  // V: each 16-lane group takes 8 d groups x 2 key groups, so both its
+  // global loads (8 lanes = one 128-byte line) and its transposed LDS writes
+  // (8 rows x 2 halves of a chunk) are conflict-free
+  const int vrest = tid >> 4;
+  const int vdg = (lane & 7) + 8 * (vrest % (CPR / 8));           // 8-wide d group
+  const int vkq = ((lane >> 3) & 1) + 2 * (vrest / (CPR / 8));    // group of KPT keys
   const uint32_t P = (uint32_t)min(a.pool_slots, (int64_t)0x7fffffff);
 
   // slot of a key of this request, clamped into the table and the pool
@@ -217,17 +228,24 @@ __global__ __launch_bounds__(256, 2) void extend_bf16(ExtendArgs a) {
     }
     return slot;
   };
-  auto gather = [&](const char* base, int32_t slot, int chunk) -> uint4 {
-    const uint64_t off = ((uint64_t)(uint32_t)slot * (uint32_t)a.hkv + (uint32_t)g) * ROWB + chunk * 16;
-    return *(const uint4*)(base + off);
+  // per-thread bases (kv head g, this thread's 16-byte chunk): a gathered
+  // row is then base + slot * slot_bytes, one 64-bit multiply-add
+  const uint32_t slot_bytes = (uint32_t)a.hkv * ROWB;
+  const char* kbase = kp + (uint64_t)g * ROWB + kc * 16;
+  const char* vbase = vp + (uint64_t)g * ROWB + vdg * 16;
+  int krel[KPASS];
+#pragma unroll
+  for (int i = 0; i < KPASS; ++i) krel[i] = key_of_row(krow + i * KROWS);
+  auto gather = [&](const char* base, int32_t slot) -> uint4 {
+    return *(const uint4*)(base + (uint64_t)(uint32_t)slot * slot_bytes);
   };
   uint4 kreg[KPASS], vreg[KPT];
   auto load_tile = [&](int tile) {
     const int32_t* sl = Sl[tile % 3];
 #pragma unroll
-    for (int i = 0; i < KPASS; ++i) kreg[i] = gather(kp, sl[key_of_row(krow + i * KROWS)], kc);
+    for (int i = 0; i < KPASS; ++i) kreg[i] = gather(kbase, sl[krel[i]]);
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) vreg[u] = gather(vp, sl[vkq * KPT + u], vdg);
+    for (int u = 0; u < KPT; ++u) vreg[u] = gather(vbase, sl[vkq * KPT + u]);
   };
   auto store_tile = [&](int buf) {
     uint16_t* ks = Ks[buf];
@@ -235,9 +253,9 @@ __global__ __launch_bounds__(256, 2) void extend_bf16(ExtendArgs a) {
 #pragma unroll
     for (int i = 0; i < KPASS; ++i)
       *(uint4*)(ks + (krow + i * KROWS) * KP + kc * 8) = kreg[i];
-    // V transposed: element (d, key) at vt[d*VP + ((key/8) ^ (d/8 & 7))*8 + key%8]
+    // V transposed: element (d, key) at vt[d*VP + vt_chunk(key/8, d)*8 + key%8]
     const int key0 = vkq * KPT;
-    const int phys = ((key0 >> 3) ^ (vdg & 7)) * 8 + (key0 & 7);
+    const int wswz = ((key0 >> 3) ^ vdg) & 7;
     const uint32_t* w32[KPT];
 #pragma unroll
     for (int u = 0; u < KPT; ++u) w32[u] = (const uint32_t*)&vreg[u];
@@ -246,6 +264,8 @@ __global__ __launch_bounds__(256, 2) void extend_bf16(ExtendArgs a) {
 #pragma unroll
       for (int hi = 0; hi < 2; ++hi) {
         const int d = vdg * 8 + e2 * 2 + hi;
+        // vt_chunk(key0/8, d) with d%8 = 2*e2 + hi and d/8 = vdg
+        const int phys = (wswz ^ (e2 * 2 + hi)) * 8 + (key0 & 7);
         uint32_t pk[2];
 #pragma unroll
         for (int u = 0; u < KPT; u += 2) {
@@ -260,6 +280,7 @@ __global__ __launch_bounds__(256, 2) void extend_bf16(ExtendArgs a) {
     }
   };
 
+  const int rswz = ((l16 & 7) ^ (l16 >> 3)) & 7;   // V^T read swizzle of this lane's rows
   // one 64-key tile: S^T = K Q^T, online softmax, O^T += V^T P^T
   auto tile_body = [&](int tile, int buf, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
@@ -297,8 +318,8 @@ __global__ __launch_bounds__(256, 2) void extend_bf16(ExtendArgs a) {
 #pragma unroll
       for (int kb = 1; kb < 4; ++kb)
         mx = fmaxf(mx, fmaxf(fmaxf(sacc[qb][kb][0], sacc[qb][kb][1]), fmaxf(sacc[qb][kb][2], sacc[qb][kb][3])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = rkv::max_xor16(mx);
+      mx = rkv::max_xor32(mx);
       const float mt = mx * c;
       if (__builtin_amdgcn_ballot_w64(mt > mref[qb] + kRescaleThreshold)) {
         const float mn = fmaxf(mref[qb], mt);
@@ -334,7 +355,8 @@ __global__ __launch_bounds__(256, 2) void extend_bf16(ExtendArgs a) {
       const int d = db * 16 + l16;
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
-        const int phys = ((cc * 4 + gq) ^ ((d >> 3) & 7)) * 8;
+        // vt_chunk(cc*4 + gq, d) with d%8 = l16%8 and d/8 = 2*db + l16/8
+        const int phys = ((cc * 4 + gq) ^ rswz ^ ((2 * db) & 7)) * 8;
         const bf16x8 va = __builtin_bit_cast(bf16x8, *(const uint4*)(vt + d * VP + phys));
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)

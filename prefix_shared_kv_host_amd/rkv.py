@@ -16,7 +16,8 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "librkv.so")
+# RKV_LIB may point at another build of the same library (for A/B timing)
+LIB_PATH = os.environ.get("RKV_LIB") or os.path.join(_HERE, "librkv.so")
 
 OK, EINVAL, ENOSPC, EBUSY, EHIP, ENOTSUP = 0, -1, -2, -3, -4, -5
 F32, BF16 = 0, 1
