@@ -33,7 +33,7 @@
 
 namespace {
 
-constexpr int kChunk = 512;     // keys per split under the default rule
+constexpr int kChunk = 256;     // keys per split under the default rule
 constexpr int kWaves = 4;
 constexpr int kMaxG = 8;        // query heads handled per workgroup
 
@@ -48,6 +48,7 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   int32_t B, hq, hkv, G, hg;      // hg = head groups of <= kMaxG per kv head
   int32_t max_seq_len;            // every length is clamped to it (<= ld)
+  int32_t hb;                     // kv heads per workgroup (a slot's contiguous run)
   int32_t splits;                 // grid extent over splits
   int32_t num_splits;             // 0 = fixed chunk rule
   float scale_log2e;              // sm_scale * log2(e)
@@ -100,175 +101,186 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float* acc, floa
   m = M;
 }
 
+// Phase 1.  Work item = (request, split, block of HB kv heads [, q-head
+// group]).  A key's rows for the HB heads are HB*D contiguous elements of the
+// slot, so the workgroup reads them as one contiguous run: lane group
+// (LPR lanes) hl handles kv head hb*HB + hl, and RPI = 256/(HB*LPR) keys are
+// read per instruction (one per row group ri, which is wave-uniform, so the
+// slot index is a scalar load).  Each lane group walks the keys of the split
+// with its own fp32 online softmax; row groups (RPI > 1) merge in LDS.
 template <typename T, int D, int G, int U>
 __global__ __launch_bounds__(256) void decode_partial(DecodeArgs a) {
   using E = Elem<T>;
   constexpr int VEC = E::kVec;
-  constexpr int LPR = D / VEC;          // lanes per row
-  constexpr int RPW = 64 / LPR;         // rows per wave instruction
+  constexpr int LPR = D / VEC;          // lanes per (slot, kv head) row
   static_assert(LPR >= 8 && LPR <= 32, "row width");
+  const int HB = a.hb;                  // kv heads per workgroup
+  const int RPI = 256 / (HB * LPR);     // keys per instruction (row groups)
 
-  const int64_t grid = gridDim.x;
-  const int64_t w = rkv::xcd_work_item(blockIdx.x, grid);
+  const int64_t w = rkv::xcd_work_item(blockIdx.x, gridDim.x);
+  // item order: (head block, sub-group) outermost, then request, then split,
+  // so neighbouring requests (siblings in the tree) share an XCD
   const int s = (int)(w % a.splits);
   int64_t rest = w / a.splits;
   const int r = (int)(rest % a.B);
   rest /= a.B;
   const int sub = (int)(rest % a.hg);
-  const int g = (int)(rest / a.hg);
-  if (g >= a.hkv) return;
+  const int hblk = (int)(rest / a.hg);
+  if (hblk * HB >= a.hkv) return;
   const int L = min(a.seq_lens[r], a.max_seq_len);
   const int chunk = split_chunk(L, a.num_splits);
   const int nsplit = (L + chunk - 1) / chunk;
   if (s >= nsplit) return;
   const int k_begin = s * chunk;
   const int k_end = min(L, k_begin + chunk);
-  const int h0 = sub * kMaxG;                  // first head of this group within the kv group
-  const int nh = min(G, a.G - h0);              // heads handled here (<= G)
+  const int h0 = sub * kMaxG;                   // first q head of this group within a kv group
+  const int nh = min(G, a.G - h0);              // q heads handled here (<= G)
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int lr = lane % LPR;                    // lane within row
-  const int rw = lane / LPR;                    // row within wave instruction
+  const int tid = threadIdx.x;
+  const int lr = tid % LPR;                     // lane within row
+  const int hl = (tid / LPR) % HB;              // kv head within the block
+  // row group; wave-uniform (scalar slot loads) when a row group spans whole waves
+  const int ri = (HB * LPR >= 64) ? __builtin_amdgcn_readfirstlane(tid / (HB * LPR)) : tid / (HB * LPR);
+  const int g = hblk * HB + hl;                 // kv head of this lane group
+  const bool gvalid = g < a.hkv;
+  const int gg = gvalid ? g : a.hkv - 1;
 
   // queries, pre-scaled into the log2 domain
   float qv[G][VEC];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const int hh = min(h, nh - 1);
-    const int64_t qoff = ((int64_t)r * a.hq + (int64_t)g * a.G + h0 + hh) * D + lr * VEC;
+  for (int hh = 0; hh < G; ++hh) {
+    const int qh = min(hh, nh - 1);
+    const int64_t qoff = ((int64_t)r * a.hq + (int64_t)gg * a.G + h0 + qh) * D + lr * VEC;
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) qv[h][e] = E::load1(a.q, qoff + e) * a.scale_log2e;
+    for (int e = 0; e < VEC; ++e) qv[hh][e] = E::load1(a.q, qoff + e) * a.scale_log2e;
   }
   float m[G], l[G], acc[G][VEC];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = -INFINITY;
-    l[h] = 0.f;
+  for (int hh = 0; hh < G; ++hh) {
+    m[hh] = -INFINITY;
+    l[hh] = 0.f;
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[h][e] = 0.f;
+    for (int e = 0; e < VEC; ++e) acc[hh][e] = 0.f;
   }
 
   const int32_t* row_tab = a.r2t + (int64_t)r * a.ld;
-  const uint4* kp = (const uint4*)a.kp;
-  const uint4* vp = (const uint4*)a.vp;
-  const int64_t slot_stride = (int64_t)a.hkv * LPR;   // uint4 per slot
-  const int64_t head_off = (int64_t)g * LPR + lr;
-  constexpr int STEP = kWaves * RPW * U;             // keys per workgroup iteration
+  const uint32_t P = (uint32_t)min(a.pool_slots, (int64_t)0x7fffffff);
+  const uint32_t slot_bytes = (uint32_t)a.hkv * D * (uint32_t)sizeof(T);
+  const char* kbase = (const char*)a.kp + ((uint64_t)gg * LPR + lr) * 16;
+  const char* vbase = (const char*)a.vp + ((uint64_t)gg * LPR + lr) * 16;
+  const int step = U * RPI;
 
-  for (int base = k_begin; base < k_end; base += STEP) {
+  // slot indices run one iteration ahead of the K/V gathers that use them
+  int32_t slots[U];
+  auto fetch_slots = [&](int base) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) slots[u] = row_tab[min(base + u * RPI + ri, k_end - 1)];
+  };
+  fetch_slots(k_begin);
+  for (int base = k_begin; base < k_end; base += step) {
     uint4 kr[U], vr[U];
     bool ok[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int key = base + (wave * U + u) * RPW + rw;
+      const int key = base + u * RPI + ri;       // wave-uniform
       ok[u] = key < k_end;
-      int32_t slot = ok[u] ? row_tab[key] : 0;
-      if (slot < 0 || (int64_t)slot >= a.pool_slots) {
-        if (ok[u]) rkv::raise_flag(a.err);
+      int32_t slot = slots[u];
+      if ((uint32_t)slot >= P) {
+        if (a.err) rkv::raise_flag(a.err);
         ok[u] = false;
         slot = 0;
       }
-      const int64_t off = (int64_t)slot * slot_stride + head_off;
-      kr[u] = ok[u] ? kp[off] : make_uint4(0, 0, 0, 0);
-      vr[u] = ok[u] ? vp[off] : make_uint4(0, 0, 0, 0);
+      const uint64_t off = (uint64_t)(uint32_t)slot * slot_bytes;
+      kr[u] = *(const uint4*)(kbase + off);
+      vr[u] = *(const uint4*)(vbase + off);
     }
+    if (base + step < k_end) fetch_slots(base + step);
     float sc[U][G];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float kf[VEC];
       E::unpack(kr[u], kf);
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
+      for (int hh = 0; hh < G; ++hh) {
         float t = 0.f;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) t = fmaf(qv[h][e], kf[e], t);
-        sc[u][h] = rkv::group_sum<LPR>(t);
+        for (int e = 0; e < VEC; ++e) t = fmaf(qv[hh][e], kf[e], t);
+        sc[u][hh] = rkv::group_sum<LPR>(t);
       }
     }
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
+    for (int hh = 0; hh < G; ++hh) {
       float mx = -INFINITY;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        if (!ok[u]) sc[u][h] = -INFINITY;
-        mx = fmaxf(mx, sc[u][h]);
+        if (!ok[u]) sc[u][hh] = -INFINITY;
+        mx = fmaxf(mx, sc[u][hh]);
       }
-      const float mn = fmaxf(m[h], mx);
+      const float mn = fmaxf(m[hh], mx);
       const float mref = (mn == -INFINITY) ? 0.f : mn;
-      const float alpha = exp2f(m[h] - mref);
-      l[h] *= alpha;
+      const float alpha = __builtin_amdgcn_exp2f(m[hh] - mref);
+      l[hh] *= alpha;
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[h][e] *= alpha;
-      m[h] = mn;
+      for (int e = 0; e < VEC; ++e) acc[hh][e] *= alpha;
+      m[hh] = mn;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const float p = exp2f(sc[u][h] - mref);
-        l[h] += p;
+        const float p = __builtin_amdgcn_exp2f(sc[u][hh] - mref);
+        l[hh] += p;
         float vf[VEC];
         E::unpack(vr[u], vf);
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
+        for (int e = 0; e < VEC; ++e) acc[hh][e] = fmaf(p, vf[e], acc[hh][e]);
       }
     }
   }
 
-  // merge the RPW row groups of this wave (lanes lr, lr+LPR, ...)
+  // row groups (RPI > 1) merge in LDS: [row group][head in block][G][D + 2]
+  extern __shared__ float red[];
+  if (RPI > 1) {
+    if (ri > 0) {
+      float* dst = red + (((ri - 1) * HB + hl) * G) * (D + 2);
 #pragma unroll
-  for (int off = LPR; off < 64; off <<= 1) {
+      for (int hh = 0; hh < G; ++hh) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float mb = __shfl_xor(m[h], off);
-      const float lb = __shfl_xor(l[h], off);
-      float ab[VEC];
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) ab[e] = __shfl_xor(acc[h][e], off);
-      merge_state(m[h], l[h], acc[h], mb, lb, ab, VEC);
+        for (int e = 0; e < VEC; ++e) dst[hh * (D + 2) + lr * VEC + e] = acc[hh][e];
+        if (lr == 0) {
+          dst[hh * (D + 2) + D] = m[hh];
+          dst[hh * (D + 2) + D + 1] = l[hh];
+        }
+      }
     }
-  }
-
-  // merge the 4 waves in LDS: [wave][head][D + 2]
-  __shared__ float red[kWaves][G][D + 2];
-  if (rw == 0) {
+    __syncthreads();
+    if (ri > 0) return;
+    for (int rr = 1; rr < RPI; ++rr) {
+      const float* src = red + (((rr - 1) * HB + hl) * G) * (D + 2);
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
+      for (int hh = 0; hh < G; ++hh) {
+        float ab[VEC];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) red[wave][h][lr * VEC + e] = acc[h][e];
-      if (lr == 0) {
-        red[wave][h][D] = m[h];
-        red[wave][h][D + 1] = l[h];
+        for (int e = 0; e < VEC; ++e) ab[e] = src[hh * (D + 2) + lr * VEC + e];
+        merge_state(m[hh], l[hh], acc[hh], src[hh * (D + 2) + D], src[hh * (D + 2) + D + 1], ab, VEC);
       }
     }
   }
-  __syncthreads();
-  if (wave != 0 || rw != 0) return;
+  if (!gvalid) return;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-#pragma unroll
-    for (int ww = 1; ww < kWaves; ++ww) {
-      float ab[VEC];
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) ab[e] = red[ww][h][lr * VEC + e];
-      merge_state(m[h], l[h], acc[h], red[ww][h][D], red[ww][h][D + 1], ab, VEC);
-    }
-  }
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    if (h >= nh) break;
-    const int head = g * a.G + h0 + h;
+  for (int hh = 0; hh < G; ++hh) {
+    if (hh >= nh) break;
+    const int head = g * a.G + h0 + hh;
     if (nsplit == 1) {
-      const float inv = 1.f / l[h];
+      const float inv = 1.f / l[hh];
       const int64_t ooff = ((int64_t)r * a.hq + head) * D + lr * VEC;
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) E::store1(a.o, ooff + e, acc[h][e] * inv);
-      if (a.lse && lr == 0) a.lse[(int64_t)r * a.hq + head] = (m[h] + log2f(l[h])) * 0.69314718055994531f;
+      for (int e = 0; e < VEC; ++e) E::store1(a.o, ooff + e, acc[hh][e] * inv);
+      if (a.lse && lr == 0) a.lse[(int64_t)r * a.hq + head] = (m[hh] + log2f(l[hh])) * 0.69314718055994531f;
     } else {
       float* dst = a.ws + (((int64_t)r * a.hq + head) * a.splits + s) * (D + 2);
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) dst[lr * VEC + e] = acc[h][e];
+      for (int e = 0; e < VEC; ++e) dst[lr * VEC + e] = acc[hh][e];
       if (lr == 0) {
-        dst[D] = m[h];
-        dst[D + 1] = l[h];
+        dst[D] = m[hh];
+        dst[D + 1] = l[hh];
       }
     }
   }
@@ -313,8 +325,11 @@ __global__ __launch_bounds__(64) void decode_merge(DecodeArgs a) {
 
 template <typename T, int D, int G>
 void launch_partial(const DecodeArgs& a, int64_t grid, hipStream_t st) {
-  constexpr int U = (G >= 8) ? 2 : (G >= 4 ? 4 : 8);
-  hipLaunchKernelGGL((decode_partial<T, D, G, U>), dim3((unsigned)grid), dim3(256), 0, st, a);
+  constexpr int U = (G >= 4) ? 2 : (G >= 2 ? 4 : 16);
+  constexpr int LPR = D / Elem<T>::kVec;
+  const int rpi = 256 / (a.hb * LPR);
+  const size_t lds = rpi > 1 ? (size_t)(rpi - 1) * a.hb * G * (D + 2) * sizeof(float) : 0;
+  hipLaunchKernelGGL((decode_partial<T, D, G, U>), dim3((unsigned)grid), dim3(256), lds, st, a);
 }
 
 template <typename T, int D>
@@ -368,13 +383,21 @@ extern "C" int rkv_attn_decode(const void* q, const void* k_pool, const void* v_
   a.B = B; a.hq = hq; a.hkv = hkv; a.G = hq / hkv;
   a.hg = (a.G + kMaxG - 1) / kMaxG;
   a.max_seq_len = max_seq_len;
+  {
+    // kv heads per workgroup: as many as fill 256 lanes (power of two), so a
+    // key's rows for them are one contiguous run of the slot
+    const int lpr = d * (dtype == RKV_BF16 ? 2 : 4) / 16;
+    int hb = 256 / lpr;
+    while (hb > 1 && hb / 2 >= hkv) hb /= 2;
+    a.hb = hb;
+  }
   a.splits = (int32_t)S;
   a.num_splits = num_splits;
   a.scale_log2e = sm_scale * 1.4426950408889634f;
   a.pool_slots = pool_slots;
   a.ws = (float*)workspace;
   if (int rc = rkv::debug_flag(&a.err)) return rc;
-  int64_t grid = (int64_t)S * B * hkv * a.hg;
+  int64_t grid = (int64_t)S * B * ((hkv + a.hb - 1) / a.hb) * a.hg;
   grid = (grid + rkv::kXcds - 1) / rkv::kXcds * rkv::kXcds;
   if (grid > 0x7fffffff) return rkv::fail(RKV_ENOTSUP, "rkv_attn_decode: grid too large");
   hipStream_t st = (hipStream_t)stream;
