@@ -99,9 +99,6 @@ __device__ bool locate_tile(const ExtendArgs& a, int64_t tg, int& r, int& t) {
   return false;
 }
 
-// Physical 16-byte chunk of logical chunk `ch` (8 keys) in V^T row d.
-__device__ __forceinline__ int vt_chunk(int ch, int d) { return ch ^ ((d ^ (d >> 3)) & 7); }
-
 // Key held by K LDS row rho of a 64-key tile.  Within each 32-key chunk,
 // rows 0..15 hold keys 8*(i/4) + i%4 and rows 16..31 hold 8*(i/4) + 4 + i%4,
 // so MFMA block kb = 2c + half gives lane group gq the keys
@@ -109,6 +106,25 @@ __device__ __forceinline__ int vt_chunk(int ch, int d) { return ch ^ ((d ^ (d >>
 __device__ __forceinline__ int key_of_row(int rho) {
   const int c = rho >> 5, rr = rho & 31, half = rr >> 4, i = rr & 15;
   return c * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+}
+
+// XOR swizzles of the 16-byte chunk index by LDS row (tiles are stored with
+// no padding, rows of D*2 bytes).  K is read as 16 consecutive rows per
+// instruction; V is read transposed, 4 rows from each of 4 lane groups
+// (rows 8 apart), and each swizzle gives the rows of one read distinct chunks.
+template <int CH>
+__device__ __forceinline__ int swz_k(int row) { return row & (CH - 1); }
+template <int CH>
+__device__ __forceinline__ int swz_v(int row) {
+  return CH == 16 ? ((row & 3) | (((row >> 3) & 3) << 2)) : ((row & 3) | (((row >> 3) & 1) << 2));
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+#define RKV_LDS __attribute__((address_space(3)))
+
+// 16-byte global -> LDS copy: lane l's bytes land at lds_base + 16*l.
+__device__ __forceinline__ void dma16(const void* g, const void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (RKV_LDS void*)lds_base, 16, 0, 0);
 }
 
 // Softmax weights are kept relative to a per-row reference maximum that is
@@ -119,26 +135,19 @@ constexpr float kRescaleThreshold = 8.0f;
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void extend_bf16(ExtendArgs a) {
-  // LDS layouts, chosen with a bank-conflict probe on gfx950: a 16-row
-  // ds_read_b128 pattern is conflict-free when the row pitch is 2 mod 4
-  // 16-byte chunks (K: D + 16 elements), or at a 128-byte pitch when the
-  // chunk index is XOR-swizzled by the row (V^T, see vt_chunk)
-  constexpr int KP = D + 16;         // K row pitch in LDS (elements)
-  constexpr int VP = BN;             // V^T row pitch in LDS (elements)
-  constexpr int KSTEPS = D / 32;     // QK contraction steps
-  constexpr int DBLK = D / 16;       // PV output blocks
-  constexpr int CPR = D / 8;         // 16-byte chunks per K/V row
-  constexpr int KROWS = 256 / CPR;   // K rows loaded per pass
-  constexpr int KPASS = BN / KROWS;  // passes per tile
-  constexpr int KPT = BN * CPR / 256;  // V keys per thread (transposed group)
-  static_assert(KPT == 2 || KPT == 4, "V transpose group");
+  constexpr int ROWB = D * 2;              // bytes of one (slot, kv head) row
+  constexpr int CH = D / 8;                // 16-byte chunks per row
+  constexpr int KSTEPS = D / 32;           // QK contraction steps
+  constexpr int DBLK = D / 16;             // PV output blocks
+  constexpr int RPI = 1024 / ROWB;         // rows one wave moves per DMA instruction
+  constexpr int NDMA = BN / (RPI * 4);     // DMA instructions per wave per tile (each of K, V)
+  constexpr int TILEB = BN * ROWB;         // bytes of one K or V tile
 
-  // two stages: the next tile is written while the current one is read;
-  // slot indices run one more tile ahead in three small stages, so a K/V
-  // gather never waits on a global index load
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VP];
-  __shared__ __attribute__((aligned(16))) int32_t Sl[3][BN];
+  // K runs one tile ahead of V (QK of tile t+1 overlaps the softmax and PV
+  // of tile t), each in two stages; slot indices run one more tile ahead
+  __shared__ __attribute__((aligned(16))) char Ks[2][TILEB];
+  __shared__ __attribute__((aligned(16))) char Vs[2][TILEB];
+  __shared__ __attribute__((aligned(16))) int32_t Sl[4][BN];
 
   const int64_t w = rkv::xcd_work_item(blockIdx.x, gridDim.x);
   const int g = (int)(w / a.tiles_bound);
@@ -202,24 +211,11 @@ __global__ __launch_bounds__(256, 2) void extend_bf16(ExtendArgs a) {
   const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
   const float c = a.scale_log2e;
 
-  // ---- tile loader: every gathered row index is clamped into [0, kv_end)
-  //      and every slot into [0, pool_slots), so no access leaves the table or
-  //      the pool; keys past kv_end are masked by the causal test.
+  // ---- gathers: every row index is clamped into [0, kv_end) and every slot
+  //      into [0, pool_slots), so no access leaves the table or the pool;
+  //      keys past kv_end are masked by the causal test
   const int32_t* row_tab = a.r2t + (int64_t)r * a.ld;
-  const char* kp = (const char*)a.kp;
-  const char* vp = (const char*)a.vp;
-  constexpr int ROWB = D * 2;          // bytes of one (slot, kv head) row
-  const int kc = tid % CPR;            // K chunk (16 bytes) this thread moves
-  const int krow = tid / CPR;          // first K LDS row this thread moves
-  // V: each 16-lane group takes 8 d groups x 2 key groups, so both its
-  // global loads (8 lanes = one 128-byte line) and its transposed LDS writes
-  // (8 rows x 2 halves of a chunk) are conflict-free
-  const int vrest = tid >> 4;
-  const int vdg = (lane & 7) + 8 * (vrest % (CPR / 8));           // 8-wide d group
-  const int vkq = ((lane >> 3) & 1) + 2 * (vrest / (CPR / 8));    // group of KPT keys
   const uint32_t P = (uint32_t)min(a.pool_slots, (int64_t)0x7fffffff);
-
-  // slot of a key of this request, clamped into the table and the pool
   auto fetch_slot = [&](int key) -> int32_t {
     int32_t slot = row_tab[min(key, kv_end - 1)];
     if ((uint32_t)slot >= P) {
@@ -228,65 +224,38 @@ __global__ __launch_bounds__(256, 2) void extend_bf16(ExtendArgs a) {
     }
     return slot;
   };
-  // per-thread bases (kv head g, this thread's 16-byte chunk): a gathered
-  // row is then base + slot * slot_bytes, one 64-bit multiply-add
   const uint32_t slot_bytes = (uint32_t)a.hkv * ROWB;
-  const char* kbase = kp + (uint64_t)g * ROWB + kc * 16;
-  const char* vbase = vp + (uint64_t)g * ROWB + vdg * 16;
-  int krel[KPASS];
+  // DMA lane roles: row (within the wave's run of RPI rows) and LDS chunk
+  const int drow = lane / CH;
+  const int dch = lane % CH;
+  const char* kg = (const char*)a.kp + (uint64_t)g * ROWB;
+  const char* vg = (const char*)a.vp + (uint64_t)g * ROWB;
+  auto dma_k = [&](int tile) {
+    const int32_t* sl = Sl[tile & 3];
+    char* dst = Ks[tile & 1];
 #pragma unroll
-  for (int i = 0; i < KPASS; ++i) krel[i] = key_of_row(krow + i * KROWS);
-  auto gather = [&](const char* base, int32_t slot) -> uint4 {
-    return *(const uint4*)(base + (uint64_t)(uint32_t)slot * slot_bytes);
+    for (int j = 0; j < NDMA; ++j) {
+      const int R = (wave * NDMA + j) * RPI + drow;
+      const int lch = dch ^ swz_k<CH>(R);
+      const int32_t slot = sl[key_of_row(R)];
+      dma16(kg + (uint64_t)(uint32_t)slot * slot_bytes + lch * 16, dst + (wave * NDMA + j) * 1024);
+    }
   };
-  uint4 kreg[KPASS], vreg[KPT];
-  auto load_tile = [&](int tile) {
-    const int32_t* sl = Sl[tile % 3];
+  auto dma_v = [&](int tile) {
+    const int32_t* sl = Sl[tile & 3];
+    char* dst = Vs[tile & 1];
 #pragma unroll
-    for (int i = 0; i < KPASS; ++i) kreg[i] = gather(kbase, sl[krel[i]]);
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) vreg[u] = gather(vbase, sl[vkq * KPT + u]);
-  };
-  auto store_tile = [&](int buf) {
-    uint16_t* ks = Ks[buf];
-    uint16_t* vt = Vt[buf];
-#pragma unroll
-    for (int i = 0; i < KPASS; ++i)
-      *(uint4*)(ks + (krow + i * KROWS) * KP + kc * 8) = kreg[i];
-    // V transposed: element (d, key) at vt[d*VP + vt_chunk(key/8, d)*8 + key%8]
-    const int key0 = vkq * KPT;
-    const int wswz = ((key0 >> 3) ^ vdg) & 7;
-    const uint32_t* w32[KPT];
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) w32[u] = (const uint32_t*)&vreg[u];
-#pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {
-#pragma unroll
-      for (int hi = 0; hi < 2; ++hi) {
-        const int d = vdg * 8 + e2 * 2 + hi;
-        // vt_chunk(key0/8, d) with d%8 = 2*e2 + hi and d/8 = vdg
-        const int phys = (wswz ^ (e2 * 2 + hi)) * 8 + (key0 & 7);
-        uint32_t pk[2];
-#pragma unroll
-        for (int u = 0; u < KPT; u += 2) {
-          const uint32_t x0 = w32[u][e2], x1 = w32[u + 1][e2];
-          pk[u / 2] = hi ? __builtin_amdgcn_perm(x1, x0, 0x07060302u) : __builtin_amdgcn_perm(x1, x0, 0x05040100u);
-        }
-        if constexpr (KPT == 4)
-          *(uint2*)(vt + d * VP + phys) = make_uint2(pk[0], pk[1]);
-        else
-          *(uint32_t*)(vt + d * VP + phys) = pk[0];
-      }
+    for (int j = 0; j < NDMA; ++j) {
+      const int R = (wave * NDMA + j) * RPI + drow;
+      const int lch = dch ^ swz_v<CH>(R);
+      const int32_t slot = sl[R];
+      dma16(vg + (uint64_t)(uint32_t)slot * slot_bytes + lch * 16, dst + (wave * NDMA + j) * 1024);
     }
   };
 
-  const int rswz = ((l16 & 7) ^ (l16 >> 3)) & 7;   // V^T read swizzle of this lane's rows
-  // one 64-key tile: S^T = K Q^T, online softmax, O^T += V^T P^T
-  auto tile_body = [&](int tile, int buf, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    const uint16_t* ks = Ks[buf];
-    const uint16_t* vt = Vt[buf];
-    f32x4 sacc[2][4];
+  // ---- S^T = K Q^T for one tile (both query blocks)
+  auto qk = [&](int tile, f32x4 (&sacc)[2][4]) {
+    const char* ks = Ks[tile & 1];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -295,15 +264,24 @@ __global__ __launch_bounds__(256, 2) void extend_bf16(ExtendArgs a) {
     for (int s = 0; s < KSTEPS; ++s) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const bf16x8 ka = __builtin_bit_cast(bf16x8, *(const uint4*)(ks + (kb * 16 + l16) * KP + s * 32 + gq * 8));
+        const int row = kb * 16 + l16;
+        const bf16x8 ka = __builtin_bit_cast(
+            bf16x8, *(const uint4*)(ks + row * ROWB + (((s * 4 + gq) ^ swz_k<CH>(row)) << 4)));
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
           sacc[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qreg[qb][s], sacc[qb][kb], 0, 0, 0);
       }
     }
-    // lane owns query l16 of each block and keys
-    //   tile*64 + 32*(kb/2) + 8*gq + 4*(kb%2) + i   (block kb, element i)
-    bf16x8 pb[2][2];
+  };
+
+  // ---- softmax of tile `tile` (scores in sacc) and O^T += V^T P^T; the QK
+  //      of the next tile is issued in the same basic block so its MFMAs
+  //      overlap this tile's exponentials
+  f32x4 s_cur[2][4], s_nxt[2][4];
+  auto step = [&](int tile, auto mask_tag, auto next_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr bool NEXT = decltype(next_tag)::value;
+    float mt[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       if constexpr (MASK) {
@@ -312,39 +290,46 @@ __global__ __launch_bounds__(256, 2) void extend_bf16(ExtendArgs a) {
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (32 * (kb >> 1) + 4 * (kb & 1) + i > lim) sacc[qb][kb][i] = -INFINITY;
+            if (32 * (kb >> 1) + 4 * (kb & 1) + i > lim) s_cur[qb][kb][i] = -INFINITY;
       }
-      float mx = fmaxf(fmaxf(sacc[qb][0][0], sacc[qb][0][1]), fmaxf(sacc[qb][0][2], sacc[qb][0][3]));
+      float mx = fmaxf(fmaxf(s_cur[qb][0][0], s_cur[qb][0][1]), fmaxf(s_cur[qb][0][2], s_cur[qb][0][3]));
 #pragma unroll
       for (int kb = 1; kb < 4; ++kb)
-        mx = fmaxf(mx, fmaxf(fmaxf(sacc[qb][kb][0], sacc[qb][kb][1]), fmaxf(sacc[qb][kb][2], sacc[qb][kb][3])));
+        mx = fmaxf(mx, fmaxf(fmaxf(s_cur[qb][kb][0], s_cur[qb][kb][1]), fmaxf(s_cur[qb][kb][2], s_cur[qb][kb][3])));
       mx = rkv::max_xor16(mx);
       mx = rkv::max_xor32(mx);
-      const float mt = mx * c;
-      if (__builtin_amdgcn_ballot_w64(mt > mref[qb] + kRescaleThreshold)) {
-        const float mn = fmaxf(mref[qb], mt);
+      mt[qb] = mx * c;
+    }
+    if (__builtin_amdgcn_ballot_w64(mt[0] > mref[0] + kRescaleThreshold ||
+                                    mt[1] > mref[1] + kRescaleThreshold)) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float mn = fmaxf(mref[qb], mt[qb]);
         const float alpha = __builtin_amdgcn_exp2f(mref[qb] - mn);
         mref[qb] = mn;
         lacc[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < DBLK; ++db) oacc[qb][db] *= alpha;
       }
+    }
+    if constexpr (NEXT) qk(tile + 1, s_nxt);
+    bf16x8 pb[2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
       const float m = mref[qb];
-      float pv[4][4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pv[kb][i] = __builtin_amdgcn_exp2f(fmaf(sacc[qb][kb][i], c, -m));
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
-        uint4 u;
-        u.x = rkv::pack_bf16x2(pv[2 * cc][0], pv[2 * cc][1]);
-        u.y = rkv::pack_bf16x2(pv[2 * cc][2], pv[2 * cc][3]);
-        u.z = rkv::pack_bf16x2(pv[2 * cc + 1][0], pv[2 * cc + 1][1]);
-        u.w = rkv::pack_bf16x2(pv[2 * cc + 1][2], pv[2 * cc + 1][3]);
-        pb[qb][cc] = __builtin_bit_cast(bf16x8, u);
+        uint32_t wv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int kb = 2 * cc + (e >> 1), i = 2 * (e & 1);
+          wv[e] = rkv::pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(s_cur[qb][kb][i], c, -m)),
+                                   __builtin_amdgcn_exp2f(fmaf(s_cur[qb][kb][i + 1], c, -m)));
+        }
+        pb[qb][cc] = __builtin_bit_cast(bf16x8, make_uint4(wv[0], wv[1], wv[2], wv[3]));
       }
     }
+    const char* vs = Vs[tile & 1];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -352,40 +337,64 @@ __global__ __launch_bounds__(256, 2) void extend_bf16(ExtendArgs a) {
         lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[qb][cc], lacc[qb], 0, 0, 0);
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) {
-      const int d = db * 16 + l16;
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
-        // vt_chunk(cc*4 + gq, d) with d%8 = l16%8 and d/8 = 2*db + l16/8
-        const int phys = ((cc * 4 + gq) ^ rswz ^ ((2 * db) & 7)) * 8;
-        const bf16x8 va = __builtin_bit_cast(bf16x8, *(const uint4*)(vt + d * VP + phys));
+        // V^T operand: two transposed reads of 4 keys each.  Lane p of group
+        // gq points at key row cc*32 + 8*gq + 4*hh + p/4, d = 16*db + 4*(p%4);
+        // lane i then receives keys [0..3] of that row run at d = 16*db + i.
+        v4i16 part[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int row = cc * 32 + gq * 8 + hh * 4 + (l16 >> 2);
+          const int d = db * 16 + 4 * (l16 & 3);
+          const char* ptr = vs + row * ROWB + ((((d >> 3) ^ swz_v<CH>(row))) << 4) + ((d & 7) << 1);
+          part[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((RKV_LDS v4i16*)ptr);
+        }
+        const bf16x8 va = __builtin_bit_cast(
+            bf16x8, make_uint4(__builtin_bit_cast(uint2, part[0]).x, __builtin_bit_cast(uint2, part[0]).y,
+                               __builtin_bit_cast(uint2, part[1]).x, __builtin_bit_cast(uint2, part[1]).y));
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
           oacc[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[qb][cc], oacc[qb][db], 0, 0, 0);
       }
     }
+    if constexpr (NEXT) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) s_cur[qb][kb] = s_nxt[qb][kb];
+    }
   };
 
-  // prologue: slots of tiles 0 and 1, then tile 0 itself
+  // prologue: slots of tiles 0..2, K of tiles 0 and 1, V of tile 0
   if (tid < BN) Sl[0][tid] = fetch_slot(tid);
-  else if (tid < 2 * BN && ntiles > 1) Sl[1][tid - BN] = fetch_slot(tid);
+  else if (tid < 2 * BN) Sl[1][tid - BN] = fetch_slot(tid);
+  else if (tid < 3 * BN) Sl[2][tid - 2 * BN] = fetch_slot(tid);
   __syncthreads();
-  load_tile(0);
-  store_tile(0);
+  dma_k(0);
+  dma_v(0);
+  if (ntiles > 1) dma_k(1);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  // iteration t: gather tile t+1 and the slots of tile t+2 while computing
-  // tile t; then publish both and meet at the barrier
+  qk(0, s_cur);
+  // iteration t (K(t+1), V(t) resident): DMA K(t+2), V(t+1) and fetch the
+  // slots of tile t+3 while computing; then publish and meet at the barrier
   for (int tile = 0; tile < ntiles; ++tile) {
-    const bool more = tile + 1 < ntiles;
-    const bool more2 = tile + 2 < ntiles;
-    if (more) load_tile(tile + 1);
+    if (tile + 2 < ntiles) dma_k(tile + 2);
+    if (tile + 1 < ntiles) dma_v(tile + 1);
     int32_t sreg = 0;
-    if (more2 && tid < BN) sreg = fetch_slot((tile + 2) * BN + tid);
-    if (tile < first_mask_tile)
-      tile_body(tile, tile & 1, std::false_type{});
-    else
-      tile_body(tile, tile & 1, std::true_type{});
-    if (more) store_tile((tile + 1) & 1);
-    if (more2 && tid < BN) Sl[(tile + 2) % 3][tid] = sreg;
+    const bool more3 = tile + 3 < ntiles;
+    if (more3 && tid < BN) sreg = fetch_slot((tile + 3) * BN + tid);
+    const bool next = tile + 1 < ntiles;
+    if (tile < first_mask_tile) {
+      if (next) step(tile, std::false_type{}, std::true_type{});
+      else step(tile, std::false_type{}, std::false_type{});
+    } else {
+      if (next) step(tile, std::true_type{}, std::true_type{});
+      else step(tile, std::true_type{}, std::false_type{});
+    }
+    if (more3 && tid < BN) Sl[(tile + 3) & 3][tid] = sreg;
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
