@@ -223,10 +223,14 @@ size_t rkv_attn_decode_workspace_bytes(int32_t B, int32_t hq, int32_t d, int32_t
  * extend).  Split-KV: the keys of a request are cut into S_r contiguous
  * chunks, each reduced to a partial (max, sum, acc) in fp32, then merged by
  * log-sum-exp rescaling.  S_r depends only on L_r and num_splits (0 = a
- * fixed chunk of 512 keys; N > 0 = at most N chunks), never on the rest of
+ * fixed chunk of 256 keys; N > 0 = at most N chunks), never on the rest of
  * the batch, so a request's output bits do not depend on its batch.  Every
  * seq_lens[r] must be <= max_seq_len and <= ld.  `workspace` (ws_bytes >=
- * rkv_attn_decode_workspace_bytes) holds the partials. */
+ * rkv_attn_decode_workspace_bytes) holds the partials.
+ * Arithmetic: fp32 FMA on the vector units; for bf16 with Hq/Hkv >= 4 the
+ * query heads of a kv head go through bf16 MFMA together (scores and PV in
+ * fp32 accumulation, weights rounded to bf16 for PV, row sums of those
+ * rounded weights, so lse is within ln(1 + 2^-8) of the exact value). */
 int rkv_attn_decode(const void* q, const void* k_pool, const void* v_pool, void* o, float* lse,
                     const int32_t* req_to_token, int64_t ld, const int32_t* seq_lens,
                     int32_t B, int32_t max_seq_len, int32_t hq, int32_t hkv, int32_t d,

@@ -53,7 +53,7 @@ struct DecodeArgs {
   int32_t num_splits;             // 0 = fixed chunk rule
   float scale_log2e;              // sm_scale * log2(e)
   int64_t pool_slots;
-  float* ws;                      // [B, hq, splits, D + 2]
+  float* ws;                      // [B, hq, splits, D + 4]: acc[D], max, sum, pad
   int* err;
 };
 
@@ -275,13 +275,223 @@ __global__ __launch_bounds__(256) void decode_partial(DecodeArgs a) {
       for (int e = 0; e < VEC; ++e) E::store1(a.o, ooff + e, acc[hh][e] * inv);
       if (a.lse && lr == 0) a.lse[(int64_t)r * a.hq + head] = (m[hh] + log2f(l[hh])) * 0.69314718055994531f;
     } else {
-      float* dst = a.ws + (((int64_t)r * a.hq + head) * a.splits + s) * (D + 2);
+      float* dst = a.ws + (((int64_t)r * a.hq + head) * a.splits + s) * (D + 4);
 #pragma unroll
       for (int e = 0; e < VEC; ++e) dst[lr * VEC + e] = acc[hh][e];
       if (lr == 0) {
         dst[D] = m[hh];
         dst[D + 1] = l[hh];
       }
+    }
+  }
+}
+
+// Phase 1 for grouped heads (bf16, Hq/Hkv >= 4): the G query heads of a kv
+// head share every K/V row, so the scores are a small matrix product.  One
+// wave per (request, kv head, split) puts the G heads in the N dimension of
+// v_mfma_f32_16x16x32_bf16 (S^T = K Q^T, 16 keys x 16 head columns, G of
+// them used) and walks the split 32 keys at a time:
+//   * each lane gathers the 16-byte pieces of its two K rows straight into
+//     MFMA A operands (registers, one step ahead);
+//   * the 32 V rows are copied global -> LDS by 16-byte DMA (two stages) and
+//     read transposed (ds_read_b64_tr_b16) as the V^T operand of O^T += V^T P^T;
+//   * K rows are assigned so that a lane's S^T accumulators hold 8 consecutive
+//     keys, which is its slice of the bf16 P^T operand;
+//   * fp32 online softmax in the log2 domain, row sums on the MFMA.
+// Memory traffic is the same as the other phase-1 kernel; the arithmetic moves
+// from VALU FMAs (8 per head per element) to the matrix cores.
+namespace gqa {
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+#define RKV_LDS __attribute__((address_space(3)))
+constexpr float kRescaleThreshold = 8.0f;
+// key (within a 32-key step) whose K row feeds MFMA row m of block kb
+__device__ __forceinline__ int key_of(int kb, int m) { return 8 * (m >> 2) + 4 * kb + (m & 3); }
+template <int CH>
+__device__ __forceinline__ int swz_v(int row) {
+  return CH == 16 ? ((row & 3) | (((row >> 3) & 3) << 2)) : ((row & 3) | (((row >> 3) & 1) << 2));
+}
+}  // namespace gqa
+
+template <int D>
+__global__ __launch_bounds__(64) void decode_gqa(DecodeArgs a) {
+  using namespace gqa;
+  constexpr int ROWB = D * 2;
+  constexpr int CH = D / 8;
+  constexpr int KSTEPS = D / 32;
+  constexpr int DBLK = D / 16;
+  constexpr int STEP = 32;
+  constexpr int RPI = 1024 / ROWB;          // V rows per DMA instruction
+  constexpr int NDMA = STEP / RPI;          // DMA instructions per step
+  __shared__ __attribute__((aligned(16))) char Vs[2][STEP * ROWB];
+
+  const int64_t w = rkv::xcd_work_item(blockIdx.x, gridDim.x);
+  const int s = (int)(w % a.splits);
+  int64_t rest = w / a.splits;
+  const int r = (int)(rest % a.B);
+  const int g = (int)(rest / a.B);
+  if (g >= a.hkv) return;
+  const int L = min(a.seq_lens[r], a.max_seq_len);
+  const int chunk = split_chunk(L, a.num_splits);
+  const int nsplit = (L + chunk - 1) / chunk;
+  if (s >= nsplit) return;
+  const int k_begin = s * chunk;
+  const int k_end = min(L, k_begin + chunk);
+
+  const int lane = threadIdx.x;
+  const int l16 = lane & 15, gq = lane >> 4;
+  const int G = a.G;
+  const bool hvalid = l16 < G;
+  const int head = g * G + (hvalid ? l16 : 0);
+
+  // Q^T operand: column l16 = query head, rows d = s*32 + 8*gq + [0..7]
+  bf16x8 qreg[KSTEPS];
+  {
+    const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)r * a.hq + head) * D + gq * 8;
+#pragma unroll
+    for (int k = 0; k < KSTEPS; ++k) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (hvalid) v = *(const uint4*)(qp + k * 32);
+      qreg[k] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  f32x4 oacc[DBLK];
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 lacc = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mref = -INFINITY;
+  const float c = a.scale_log2e;
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+
+  const int32_t* row_tab = a.r2t + (int64_t)r * a.ld;
+  const uint32_t P = (uint32_t)min(a.pool_slots, (int64_t)0x7fffffff);
+  const uint32_t slot_bytes = (uint32_t)a.hkv * ROWB;
+  const char* kg = (const char*)a.kp + (uint64_t)g * ROWB + gq * 16;
+  const char* vg = (const char*)a.vp + (uint64_t)g * ROWB;
+  // lane (lane & 31) holds the slot of key base + (lane & 31); clamped into
+  // the split and into the pool, so every gather stays in bounds
+  auto fetch = [&](int base) -> int32_t {
+    int32_t slot = row_tab[min(base + (lane & 31), k_end - 1)];
+    if ((uint32_t)slot >= P) {
+      if (a.err) rkv::raise_flag(a.err);
+      slot = 0;
+    }
+    return slot;
+  };
+  uint4 kreg[2][KSTEPS];
+  auto load_k = [&](int32_t slots) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int32_t sl = __shfl(slots, key_of(kb, l16));
+      const char* rowp = kg + (uint64_t)(uint32_t)sl * slot_bytes;
+#pragma unroll
+      for (int k = 0; k < KSTEPS; ++k) kreg[kb][k] = *(const uint4*)(rowp + k * 64);
+    }
+  };
+  auto dma_v = [&](int32_t slots, int stage) {
+    const int drow = lane / CH, dch = lane % CH;
+#pragma unroll
+    for (int j = 0; j < NDMA; ++j) {
+      const int R = j * RPI + drow;
+      const int32_t sl = __shfl(slots, R);
+      const int lch = dch ^ swz_v<CH>(R);
+      __builtin_amdgcn_global_load_lds((const void*)(vg + (uint64_t)(uint32_t)sl * slot_bytes + lch * 16),
+                                       (RKV_LDS void*)(Vs[stage] + j * 1024), 16, 0, 0);
+    }
+  };
+
+  int32_t slots = fetch(k_begin);
+  load_k(slots);
+  dma_v(slots, 0);
+  int stage = 0;
+  for (int base = k_begin; base < k_end; base += STEP) {
+    __builtin_amdgcn_s_waitcnt(0);          // K operands and this step's V tile are in
+    bf16x8 ka[2][KSTEPS];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int k = 0; k < KSTEPS; ++k) ka[kb][k] = __builtin_bit_cast(bf16x8, kreg[kb][k]);
+    const bool more = base + STEP < k_end;
+    if (more) {
+      slots = fetch(base + STEP);
+      load_k(slots);
+      dma_v(slots, stage ^ 1);
+    }
+    f32x4 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < KSTEPS; ++k)
+        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb][k], qreg[k], sacc[kb], 0, 0, 0);
+    }
+    // lane (head l16, group gq) holds keys base + 8*gq + 4*kb + i
+    const int lim = k_end - 1 - base - 8 * gq;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * kb + i > lim) sacc[kb][i] = -INFINITY;
+    float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
+                     fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
+    mx = rkv::max_xor16(mx);
+    mx = rkv::max_xor32(mx);
+    const float mt = mx * c;
+    if (__builtin_amdgcn_ballot_w64(mt > mref + kRescaleThreshold)) {
+      const float mn = fmaxf(mref, mt);
+      const float alpha = __builtin_amdgcn_exp2f(mref - mn);
+      mref = mn;
+      lacc *= alpha;
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) oacc[db] *= alpha;
+    }
+    uint32_t wv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int kb = e >> 1, i = 2 * (e & 1);
+      wv[e] = rkv::pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c, -mref)),
+                               __builtin_amdgcn_exp2f(fmaf(sacc[kb][i + 1], c, -mref)));
+    }
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(wv[0], wv[1], wv[2], wv[3]));
+    lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb, lacc, 0, 0, 0);
+    const char* vs = Vs[stage];
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) {
+      v4i16 part[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int row = gq * 8 + hh * 4 + (l16 >> 2);
+        const int d = db * 16 + 4 * (l16 & 3);
+        const char* ptr = vs + row * ROWB + (((d >> 3) ^ swz_v<CH>(row)) << 4) + ((d & 7) << 1);
+        part[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((RKV_LDS v4i16*)ptr);
+      }
+      const bf16x8 va = __builtin_bit_cast(
+          bf16x8, make_uint4(__builtin_bit_cast(uint2, part[0]).x, __builtin_bit_cast(uint2, part[0]).y,
+                             __builtin_bit_cast(uint2, part[1]).x, __builtin_bit_cast(uint2, part[1]).y));
+      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, oacc[db], 0, 0, 0);
+    }
+    stage ^= 1;
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  if (!hvalid) return;
+  // lane (head l16, group gq) holds d = db*16 + 4*gq + [0..3]
+  const float lsum = lacc[0];
+  if (nsplit == 1) {
+    const float inv = 1.f / lsum;
+    uint16_t* orow = (uint16_t*)a.o + ((int64_t)r * a.hq + head) * D;
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db)
+      *(uint2*)(orow + db * 16 + 4 * gq) = make_uint2(rkv::pack_bf16x2(oacc[db][0] * inv, oacc[db][1] * inv),
+                                                      rkv::pack_bf16x2(oacc[db][2] * inv, oacc[db][3] * inv));
+    if (a.lse && gq == 0) a.lse[(int64_t)r * a.hq + head] = (mref + log2f(lsum)) * 0.69314718055994531f;
+  } else {
+    float* dst = a.ws + (((int64_t)r * a.hq + head) * a.splits + s) * (D + 4);
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) *(f32x4*)(dst + db * 16 + 4 * gq) = oacc[db];
+    if (gq == 0) {
+      dst[D] = mref;
+      dst[D + 1] = lsum;
     }
   }
 }
@@ -298,9 +508,9 @@ __global__ __launch_bounds__(64) void decode_merge(DecodeArgs a) {
   const int nsplit = (L + chunk - 1) / chunk;
   if (nsplit <= 1) return;
   const int lane = threadIdx.x;
-  const float* src = a.ws + ((int64_t)r * a.hq + head) * a.splits * (D + 2);
+  const float* src = a.ws + ((int64_t)r * a.hq + head) * a.splits * (D + 4);
   float M = -INFINITY;
-  for (int s = lane; s < nsplit; s += 64) M = fmaxf(M, src[(int64_t)s * (D + 2) + D]);
+  for (int s = lane; s < nsplit; s += 64) M = fmaxf(M, src[(int64_t)s * (D + 4) + D]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   constexpr int PER = D / 64;
@@ -309,7 +519,7 @@ __global__ __launch_bounds__(64) void decode_merge(DecodeArgs a) {
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
   float lsum = 0.f;
   for (int s = 0; s < nsplit; ++s) {
-    const float* p = src + (int64_t)s * (D + 2);
+    const float* p = src + (int64_t)s * (D + 4);
     const float ms = p[D];
     const float f = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
     lsum += p[D + 1] * f;
@@ -334,6 +544,16 @@ void launch_partial(const DecodeArgs& a, int64_t grid, hipStream_t st) {
 
 template <typename T, int D>
 void launch_all(const DecodeArgs& a, int64_t grid, hipStream_t st) {
+  if constexpr (sizeof(T) == 2) {
+    if (a.G >= 4) {
+      // grouped heads: matrix cores, one wave per (request, kv head, split)
+      int64_t g2 = (int64_t)a.splits * a.B * a.hkv;
+      g2 = (g2 + rkv::kXcds - 1) / rkv::kXcds * rkv::kXcds;
+      hipLaunchKernelGGL((decode_gqa<D>), dim3((unsigned)g2), dim3(64), 0, st, a);
+      hipLaunchKernelGGL((decode_merge<T, D>), dim3((unsigned)((int64_t)a.B * a.hq)), dim3(64), 0, st, a);
+      return;
+    }
+  }
   const int g = a.G < kMaxG ? a.G : kMaxG;
   if (g <= 1) launch_partial<T, D, 1>(a, grid, st);
   else if (g <= 2) launch_partial<T, D, 2>(a, grid, st);
@@ -353,7 +573,7 @@ extern "C" size_t rkv_attn_decode_workspace_bytes(int32_t B, int32_t hq, int32_t
                                                   int32_t num_splits) {
   if (B < 0 || hq < 1 || (d != 64 && d != 128) || max_seq_len < 1 || num_splits < 0) return 0;
   const int64_t S = splits_extent(max_seq_len, num_splits);
-  return (size_t)B * hq * S * (d + 2) * sizeof(float);
+  return (size_t)B * hq * S * (d + 4) * sizeof(float);
 }
 
 extern "C" int rkv_attn_decode(const void* q, const void* k_pool, const void* v_pool, void* o, float* lse,

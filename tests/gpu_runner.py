@@ -20,9 +20,11 @@ from oracle.pool import OraclePool, scatter as oscatter
 from oracle.radix import OracleTree
 
 TOL = {"f32": 1e-5, "bf16": 2e-2}
-# bf16 extend sums the same bf16-rounded weights that PV uses, so its lse
-# carries their rounding: |ln(sum p^) - ln(sum p)| <= ln(1 + 2^-8) < 3.9e-3
-# (unit roundoff of bf16).  fp32 paths and decode keep fp32 weights.
+# bf16 extend, and bf16 decode with >= 4 query heads per kv head (both on
+# matrix cores), sum the same bf16-rounded weights that PV uses, so their lse
+# carries that rounding: |ln(sum p^) - ln(sum p)| <= ln(1 + 2^-8) < 3.9e-3
+# (unit roundoff of bf16).  fp32 paths and the vector-unit decode keep fp32
+# weights.
 LSE_TOL = {"f32": 1e-5, "bf16": 3.9e-3}
 
 

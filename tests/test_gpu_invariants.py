@@ -99,7 +99,9 @@ def test_decode_independent_of_num_splits():
         err = (o[0].float() - ref[0].float()).abs().max().item()
         lerr = (o[1] - ref[1]).abs().max().item()
         G.log(f"num_splits {ns}: max |o - o(1 split)| = {err:.3e}, lse {lerr:.3e}")
-        assert err <= 2e-2 and lerr <= 1e-4
+        # this shape (8 q heads per 2 kv heads) takes the matrix-core path,
+        # whose lse sums bf16-rounded weights: bound ln(1 + 2^-8)
+        assert err <= 2e-2 and lerr <= 3.9e-3
 
 
 def test_extend_with_one_token_equals_decode():

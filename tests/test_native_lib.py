@@ -46,4 +46,6 @@ def test_host_argument_errors():
         t.batch_prepare([[1, 2], []])
     L = rkv.lib()
     assert L.rkv_attn_decode_workspace_bytes(4, 8, 96, 100, 0) == 0   # unsupported D
-    assert L.rkv_attn_decode_workspace_bytes(4, 8, 128, 1024, 0) == 4 * 8 * 2 * 130 * 4
+    # B * Hq * splits(1024 keys / 256 per split) * (D + 4) floats
+    assert L.rkv_attn_decode_workspace_bytes(4, 8, 128, 1024, 0) == 4 * 8 * 4 * 132 * 4
+    assert L.rkv_attn_decode_workspace_bytes(4, 8, 128, 1024, 3) == 4 * 8 * 3 * 132 * 4
