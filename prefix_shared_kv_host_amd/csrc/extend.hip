@@ -110,21 +110,27 @@ __device__ __forceinline__ int key_of_row(int rho) {
 
 // XOR swizzles of the 16-byte chunk index by LDS row (tiles are stored with
 // no padding, rows of D*2 bytes).  K is read as 16 consecutive rows per
-// instruction; V is read transposed, 4 rows from each of 4 lane groups
-// (rows 8 apart), and each swizzle gives the rows of one read distinct chunks.
+// instruction, one chunk each: XOR by the row spreads them over all chunks.
+// V is read transposed: each 16-lane group reads one 32-byte chunk pair from
+// each of 4 consecutive rows, the 4 groups rows 8 apart; XOR of the pair
+// index by the row's low bits (and bit 3) puts the 4 rows of a group on
+// distinct banks and every bank of the wave's 512 bytes under exactly two.
 template <int CH>
 __device__ __forceinline__ int swz_k(int row) { return row & (CH - 1); }
 template <int CH>
 __device__ __forceinline__ int swz_v(int row) {
-  return CH == 16 ? ((row & 3) | (((row >> 3) & 3) << 2)) : ((row & 3) | (((row >> 3) & 1) << 2));
+  return CH == 16 ? (((row & 3) << 1) | (((row >> 3) & 1) << 3)) : ((row & 2) | (((row >> 3) & 1) << 2));
 }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 #define RKV_LDS __attribute__((address_space(3)))
 
-// 16-byte global -> LDS copy: lane l's bytes land at lds_base + 16*l.
+// Global -> LDS copies: lane l's 16 (4) bytes land at lds_base + 16*l (4*l).
 __device__ __forceinline__ void dma16(const void* g, const void* lds_base) {
   __builtin_amdgcn_global_load_lds(g, (RKV_LDS void*)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, const void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (RKV_LDS void*)lds_base, 4, 0, 0);
 }
 
 // Softmax weights are kept relative to a per-row reference maximum that is
@@ -144,10 +150,27 @@ __global__ __launch_bounds__(256, 2) void extend_bf16(ExtendArgs a) {
   constexpr int TILEB = BN * ROWB;         // bytes of one K or V tile
 
   // K runs one tile ahead of V (QK of tile t+1 overlaps the softmax and PV
-  // of tile t), each in two stages; slot indices run one more tile ahead
-  __shared__ __attribute__((aligned(16))) char Ks[2][TILEB];
-  __shared__ __attribute__((aligned(16))) char Vs[2][TILEB];
-  __shared__ __attribute__((aligned(16))) int32_t Sl[4][BN];
+  // of tile t), each in two stages; slot indices run one more tile ahead.
+  // The stages are separate LDS objects addressed with a compile-time parity
+  // (the key loop is unrolled by two), so the compiler can tell that the
+  // operand reads of one stage never alias the DMA still writing the other
+  // and does not wait for that DMA before them.
+  __shared__ __attribute__((aligned(16))) char K0[TILEB];
+  __shared__ __attribute__((aligned(16))) char K1[TILEB];
+  __shared__ __attribute__((aligned(16))) char V0[TILEB];
+  __shared__ __attribute__((aligned(16))) char V1[TILEB];
+  // slot indices of four tiles, stored in the order the gather lanes use
+  // them (each lane's NDMA slots of a tile are contiguous: one LDS read)
+  __shared__ __attribute__((aligned(16))) int32_t SlK[4][BN];
+  __shared__ __attribute__((aligned(16))) int32_t SlV[4][BN];
+  auto kbuf = [&](auto par) -> char* {
+    if constexpr (decltype(par)::value == 0) return K0; else return K1;
+  };
+  auto vbuf = [&](auto par) -> char* {
+    if constexpr (decltype(par)::value == 0) return V0; else return V1;
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
 
   const int64_t w = rkv::xcd_work_item(blockIdx.x, gridDim.x);
   const int g = (int)(w / a.tiles_bound);
@@ -216,46 +239,74 @@ __global__ __launch_bounds__(256, 2) void extend_bf16(ExtendArgs a) {
   //      keys past kv_end are masked by the causal test
   const int32_t* row_tab = a.r2t + (int64_t)r * a.ld;
   const uint32_t P = (uint32_t)min(a.pool_slots, (int64_t)0x7fffffff);
-  auto fetch_slot = [&](int key) -> int32_t {
-    int32_t slot = row_tab[min(key, kv_end - 1)];
-    if ((uint32_t)slot >= P) {
-      if (a.err) rkv::raise_flag(a.err);
-      slot = 0;
-    }
-    return slot;
-  };
   const uint32_t slot_bytes = (uint32_t)a.hkv * ROWB;
+  bool bad = false;   // some gathered slot was outside the pool
   // DMA lane roles: row (within the wave's run of RPI rows) and LDS chunk
   const int drow = lane / CH;
   const int dch = lane % CH;
+  // LDS tile row handled by DMA instruction j of (wave w, lane row dr)
+  auto dma_row = [](int w, int j, int dr) { return (w * NDMA + j) * RPI + dr; };
+  // slot-table position p <-> (wave, lane row, instruction): the key whose
+  // slot a gather lane needs, for the K tile (rows permuted) and the V tile
+  auto pos_row = [&](int p) { return dma_row(p / (NDMA * RPI), p % NDMA, (p / NDMA) % RPI); };
+  const int key_k = key_of_row(pos_row(lane));
+  const int key_v = pos_row(lane);
   const char* kg = (const char*)a.kp + (uint64_t)g * ROWB;
   const char* vg = (const char*)a.vp + (uint64_t)g * ROWB;
-  auto dma_k = [&](int tile) {
-    const int32_t* sl = Sl[tile & 3];
-    char* dst = Ks[tile & 1];
+  // gathers of one tile; slots outside [0, pool_slots) are replaced by 0 and
+  // reported through the return value
+  auto gather = [&](const int32_t* slots, char* dst, const char* src, auto is_k) -> bool {
+    int32_t sv[NDMA];
+    const int32_t* mine = slots + (wave * RPI + drow) * NDMA;
+    if constexpr (NDMA == 4) {
+      const int4 v = *(const int4*)mine;
+      sv[0] = v.x; sv[1] = v.y; sv[2] = v.z; sv[3] = v.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < NDMA; ++j) sv[j] = mine[j];
+    }
+    bool bad = false;
 #pragma unroll
     for (int j = 0; j < NDMA; ++j) {
-      const int R = (wave * NDMA + j) * RPI + drow;
-      const int lch = dch ^ swz_k<CH>(R);
-      const int32_t slot = sl[key_of_row(R)];
-      dma16(kg + (uint64_t)(uint32_t)slot * slot_bytes + lch * 16, dst + (wave * NDMA + j) * 1024);
+      const bool ok = (uint32_t)sv[j] < P;
+      bad |= !ok;
+      const uint32_t slot = ok ? (uint32_t)sv[j] : 0u;
+      const int R = dma_row(wave, j, drow);
+      const int lch = dch ^ (decltype(is_k)::value ? swz_k<CH>(R) : swz_v<CH>(R));
+      dma16(src + (uint64_t)slot * slot_bytes + lch * 16, dst + (wave * NDMA + j) * 1024);
     }
+    return bad;
   };
-  auto dma_v = [&](int tile) {
-    const int32_t* sl = Sl[tile & 3];
-    char* dst = Vs[tile & 1];
-#pragma unroll
-    for (int j = 0; j < NDMA; ++j) {
-      const int R = (wave * NDMA + j) * RPI + drow;
-      const int lch = dch ^ swz_v<CH>(R);
-      const int32_t slot = sl[R];
-      dma16(vg + (uint64_t)(uint32_t)slot * slot_bytes + lch * 16, dst + (wave * NDMA + j) * 1024);
-    }
+  auto dma_k = [&](int tile, auto par) { return gather(SlK[tile & 3], kbuf(par), kg, std::true_type{}); };
+  auto dma_v = [&](int tile, auto par) { return gather(SlV[tile & 3], vbuf(par), vg, std::false_type{}); };
+  // gather instruction j alone (slot read from LDS just before it), so the
+  // gathers of a tile can be spread over the MFMA work instead of queueing
+  // behind one another at the start of an iteration
+  auto gather1 = [&](const int32_t* slots, char* dst, const char* src, int j, auto is_k) -> bool {
+    const int32_t sv = slots[(wave * RPI + drow) * NDMA + j];
+    const bool ok = (uint32_t)sv < P;
+    const uint32_t slot = ok ? (uint32_t)sv : 0u;
+    const int R = dma_row(wave, j, drow);
+    const int lch = dch ^ (decltype(is_k)::value ? swz_k<CH>(R) : swz_v<CH>(R));
+    dma16(src + (uint64_t)slot * slot_bytes + lch * 16, dst + (wave * NDMA + j) * 1024);
+    return !ok;
+  };
+  // slot indices of tile `tile` into stage tile & 3 (waves 0 and 1, one
+  // 4-byte DMA each, straight from the table; clamped keys past the end)
+  auto dma_slots = [&](int tile) {
+    if (wave == 0) dma4(row_tab + min(tile * BN + key_k, kv_end - 1), SlK[tile & 3]);
+    else if (wave == 1) dma4(row_tab + min(tile * BN + key_v, kv_end - 1), SlV[tile & 3]);
   };
 
   // ---- S^T = K Q^T for one tile (both query blocks)
-  auto qk = [&](int tile, f32x4 (&sacc)[2][4]) {
-    const char* ks = Ks[tile & 1];
+  // With gathers on, contraction step s is followed by gather instruction s
+  // of K(gk) (into the stage of parity gpar) and of V(gk - 1) (the other
+  // stage); KSTEPS == NDMA for 64-key tiles.
+  static_assert(KSTEPS == NDMA, "one K and one V gather per contraction step");
+  auto qk = [&](auto par, f32x4 (&sacc)[2][4], auto gather_tag, int gk) {
+    constexpr bool GATHER = decltype(gather_tag)::value;
+    using GPAR = std::integral_constant<int, 1 - decltype(par)::value>;
+    const char* ks = kbuf(par);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -271,16 +322,26 @@ __global__ __launch_bounds__(256, 2) void extend_bf16(ExtendArgs a) {
         for (int qb = 0; qb < 2; ++qb)
           sacc[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qreg[qb][s], sacc[qb][kb], 0, 0, 0);
       }
+      if constexpr (GATHER) {
+        bad |= gather1(SlK[gk & 3], kbuf(GPAR{}), kg, s, std::true_type{});
+        bad |= gather1(SlV[(gk - 1) & 3], vbuf(par), vg, s, std::false_type{});
+      }
     }
   };
 
   // ---- softmax of tile `tile` (scores in sacc) and O^T += V^T P^T; the QK
   //      of the next tile is issued in the same basic block so its MFMAs
   //      overlap this tile's exponentials
-  f32x4 s_cur[2][4], s_nxt[2][4];
-  auto step = [&](int tile, auto mask_tag, auto next_tag) {
+  // scores of the tile being finished and of the next one; the two buffers
+  // swap roles with the tile parity, so no copy is needed between tiles
+  f32x4 s_even[2][4], s_odd[2][4];
+  auto step = [&](int tile, auto par, auto mask_tag, auto next_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
     constexpr bool NEXT = decltype(next_tag)::value;
+    using NPAR = std::integral_constant<int, 1 - decltype(par)::value>;
+    constexpr bool EVEN = decltype(par)::value == 0;
+    f32x4 (&s_cur)[2][4] = EVEN ? s_even : s_odd;
+    f32x4 (&s_nxt)[2][4] = EVEN ? s_odd : s_even;
     float mt[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -312,7 +373,9 @@ __global__ __launch_bounds__(256, 2) void extend_bf16(ExtendArgs a) {
         for (int db = 0; db < DBLK; ++db) oacc[qb][db] *= alpha;
       }
     }
-    if constexpr (NEXT) qk(tile + 1, s_nxt);
+    // QK of the next tile, with the gathers of K(t+2) and V(t+1) spread
+    // over its contraction steps
+    if constexpr (NEXT) qk(NPAR{}, s_nxt, std::true_type{}, tile + 2);
     bf16x8 pb[2][2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -329,7 +392,7 @@ __global__ __launch_bounds__(256, 2) void extend_bf16(ExtendArgs a) {
         pb[qb][cc] = __builtin_bit_cast(bf16x8, make_uint4(wv[0], wv[1], wv[2], wv[3]));
       }
     }
-    const char* vs = Vs[tile & 1];
+    const char* vs = vbuf(par);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -358,45 +421,46 @@ __global__ __launch_bounds__(256, 2) void extend_bf16(ExtendArgs a) {
           oacc[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[qb][cc], oacc[qb][db], 0, 0, 0);
       }
     }
-    if constexpr (NEXT) {
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) s_cur[qb][kb] = s_nxt[qb][kb];
-    }
   };
 
   // prologue: slots of tiles 0..2, K of tiles 0 and 1, V of tile 0
-  if (tid < BN) Sl[0][tid] = fetch_slot(tid);
-  else if (tid < 2 * BN) Sl[1][tid - BN] = fetch_slot(tid);
-  else if (tid < 3 * BN) Sl[2][tid - 2 * BN] = fetch_slot(tid);
-  __syncthreads();
-  dma_k(0);
-  dma_v(0);
-  if (ntiles > 1) dma_k(1);
+  dma_slots(0);
+  dma_slots(1);
+  dma_slots(2);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  qk(0, s_cur);
-  // iteration t (K(t+1), V(t) resident): DMA K(t+2), V(t+1) and fetch the
-  // slots of tile t+3 while computing; then publish and meet at the barrier
-  for (int tile = 0; tile < ntiles; ++tile) {
-    if (tile + 2 < ntiles) dma_k(tile + 2);
-    if (tile + 1 < ntiles) dma_v(tile + 1);
-    int32_t sreg = 0;
-    const bool more3 = tile + 3 < ntiles;
-    if (more3 && tid < BN) sreg = fetch_slot((tile + 3) * BN + tid);
+  bad |= dma_k(0, I0{});
+  bad |= dma_v(0, I0{});
+  bad |= dma_k(1, I1{});
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  qk(I0{}, s_even, std::false_type{}, 0);
+  // iteration t (K(t+1), V(t) resident): DMA K(t+2), V(t+1) and the slots
+  // of tile t+3 while computing; then wait for them and meet at the barrier
+  auto iteration = [&](int tile, auto par) {
+    using NPAR = std::integral_constant<int, 1 - decltype(par)::value>;
+    // The slot indices of tile t+3 go straight from the table into their
+    // LDS stage (wave 0, one 4-byte DMA; they are range-checked where the
+    // gathers read them), so no register has to wait for them.  Past the
+    // last tile the keys are clamped: the gathers then refill the stage
+    // consumed in the previous iteration with rows nobody reads again.
+    dma_slots(tile + 3);
     const bool next = tile + 1 < ntiles;
     if (tile < first_mask_tile) {
-      if (next) step(tile, std::false_type{}, std::true_type{});
-      else step(tile, std::false_type{}, std::false_type{});
+      if (next) step(tile, par, std::false_type{}, std::true_type{});
+      else step(tile, par, std::false_type{}, std::false_type{});
     } else {
-      if (next) step(tile, std::true_type{}, std::true_type{});
-      else step(tile, std::true_type{}, std::false_type{});
+      if (next) step(tile, par, std::true_type{}, std::true_type{});
+      else step(tile, par, std::true_type{}, std::false_type{});
     }
-    if (more3 && tid < BN) Sl[(tile + 3) & 3][tid] = sreg;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  };
+  for (int tile = 0; tile < ntiles; tile += 2) {
+    iteration(tile, I0{});
+    if (tile + 1 < ntiles) iteration(tile + 1, I1{});
   }
+  if (a.err && bad) rkv::raise_flag(a.err);
 
   // ---- epilogue: lane holds o[query l16][d = db*16 + 4*gq + 0..3]
   uint16_t* obase = (uint16_t*)a.o;

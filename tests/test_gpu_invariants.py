@@ -139,9 +139,36 @@ print("CLEAN-OK")
 """
 
 
-def test_debug_mode_flags_out_of_range_slot():
+_DEBUG_EXTEND_SCRIPT = r"""
+import sys, torch
+sys.path.insert(0, sys.argv[1])
+from prefix_shared_kv_host_amd import rkv
+P, hkv, d, hq = 512, 2, 128, 8
+kp = torch.zeros(P, hkv, d, dtype=torch.bfloat16, device="cuda")
+vp = torch.zeros_like(kp)
+# two requests: 200 cached + 70 new, 0 cached + 5 new; one bad slot deep in
+# the first request's prefix (a later tile, reached through the gathers)
+pl = torch.tensor([200, 0], dtype=torch.int32, device="cuda")
+qo = torch.tensor([0, 70, 75], dtype=torch.int32, device="cuda")
+r2t = torch.arange(2 * 270, dtype=torch.int32).view(2, 270) % P
+bad = r2t.clone(); bad[0, 130] = 10**6
+q = torch.zeros(75, hq, d, dtype=torch.bfloat16, device="cuda")
+o = torch.empty_like(q)
+try:
+    rkv.attn_extend(q, kp, vp, o, bad.cuda(), qo, pl, max_new=70)
+    print("NO-ERROR")
+except rkv.RkvError as e:
+    print("CODE", e.code)
+rkv.attn_extend(q, kp, vp, o, r2t.cuda(), qo, pl, max_new=70)
+torch.cuda.synchronize()
+print("CLEAN-OK")
+"""
+
+
+@pytest.mark.parametrize("script", [_DEBUG_SCRIPT, _DEBUG_EXTEND_SCRIPT], ids=["decode", "extend"])
+def test_debug_mode_flags_out_of_range_slot(script):
     env = dict(os.environ, RKV_DEBUG="1")
-    p = subprocess.run([sys.executable, "-c", _DEBUG_SCRIPT, ROOT], env=env, capture_output=True,
+    p = subprocess.run([sys.executable, "-c", script, ROOT], env=env, capture_output=True,
                        text=True, timeout=180)
     G.log(p.stdout + p.stderr[-2000:])
     assert "CODE -1" in p.stdout and "CLEAN-OK" in p.stdout
