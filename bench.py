@@ -56,6 +56,25 @@ def scatter_bytes(T, hkv, d, b):
     return float(4 * T * hkv * d * b + 4 * T)
 
 
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    record (profiles/hbm_traffic.json), or None when the record is missing or
+    was taken on kernel sources that have changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        rec = json.load(open(path))["kernels"][kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    m = hashlib.sha256()
+    for src in rec["sources"]:
+        try:
+            m.update(open(os.path.join(ROOT, src), "rb").read())
+        except OSError:
+            return None
+    return float(rec["bytes_per_launch"]) if m.hexdigest() == rec["sources_sha256"] else None
+
+
 class Phase:
     """A prepared batch whose tables and new-token K/V/Q sit in HBM."""
 
@@ -302,9 +321,11 @@ def main():
                       frac_of_peak_unique=dec_gbs_u / PEAK_HBM_GBS,
                       tokens_per_s=T_d / ((kern_ms[2] + kern_ms[3]) * 1e-3), scatter_us=kern_ms[2] * 1e3)
     roof_e = dict(kernel="attn_extend", bound="mfma", achieved=ext_tflops, peak=PEAK_BF16_TFLOPS,
-                  unit="TFLOP/s", frac=ext_tflops / PEAK_BF16_TFLOPS, traffic=None)
+                  unit="TFLOP/s", frac=ext_tflops / PEAK_BF16_TFLOPS, traffic=measured_traffic("attn_extend"))
+    # traffic: bytes past L2 per launch (counters, calibrated), vs algorithmic
+    # Bl; achieved counts the algorithmic (logical) bytes
     roof_d = dict(kernel="attn_decode", bound="hbm", achieved=dec_gbs, peak=PEAK_HBM_GBS, unit="GB/s",
-                  frac=dec_gbs / PEAK_HBM_GBS, traffic=None)
+                  frac=dec_gbs / PEAK_HBM_GBS, traffic=measured_traffic("attn_decode"), algorithmic_bytes=Bl)
     dominant_is_decode = kern_ms[3] >= kern_ms[1]
     out = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
