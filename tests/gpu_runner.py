@@ -7,6 +7,7 @@ asserted bit-exact against the library's), and computes attention in float64.
 """
 from __future__ import annotations
 
+import inspect
 import math
 import sys
 import time
@@ -33,6 +34,15 @@ def log(msg):
     sys.stdout.flush()
 
 
+def _pick(select, i, B, tables):
+    """Requests of phase i to check: select(i, B) or, for selectors that
+    take a third argument, select(i, B, tables) with the oracle's tables of
+    that batch (None = all)."""
+    if len(inspect.signature(select).parameters) >= 3:
+        return select(i, B, tables)
+    return select(i, B)
+
+
 def needed_slots(shape, phases, select):
     """Dry run of the oracle tree: slots the selected requests will read."""
     t = OracleTree(shape.pool, configs.free_list(shape.pool, shape.seed))
@@ -40,7 +50,7 @@ def needed_slots(shape, phases, select):
     for i, ph in enumerate(phases):
         st, tb = t.batch_prepare(ph.seqs)
         assert st == 0
-        reqs = select(i, len(ph.seqs)) if ph.kind in ("extend", "decode") else []
+        reqs = _pick(select, i, len(ph.seqs), tb) if ph.kind in ("extend", "decode") else []
         if reqs is None:
             reqs = range(len(ph.seqs))
         for r in reqs:
@@ -75,7 +85,7 @@ def run(shape, phases, select=lambda i, B: None, num_splits=0, content_device="c
         for r in range(len(ph.seqs)):
             L = otb["seq_lens"][r]
             assert list(otb["req_to_token"][r][:L]) == batch.host["req_to_token"][r][:L].tolist()
-        reqs = select(i, len(ph.seqs)) if ph.kind in ("extend", "decode") else []
+        reqs = _pick(select, i, len(ph.seqs), otb) if ph.kind in ("extend", "decode") else []
         attend = reqs is None or len(reqs) > 0
         q, k, v = content.batch_rows(shape.seed, ph.seqs, otb["prefix_lens"], shape.hq, shape.hkv,
                                      shape.d, dt, content_device, shape.q_scale, with_q=attend)

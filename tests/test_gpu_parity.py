@@ -84,6 +84,44 @@ def test_extend_c4_subset():
     G.check(res, "bf16", "c4-extend")
 
 
+def chat_selector(name, per_batch, seed=5):
+    """c5 / c5e: a seeded sample of `per_batch` turns of every batch, plus
+    every turn whose cached history was (partly) evicted and is recomputed.
+    Returns (shape, phases, selector, recompute_turns)."""
+    shape, phases = configs.build(name)
+    batches, tags = configs.chat_trace(shape.seed)
+    assert len(batches) == len(phases)
+    seqlen = {st: len(seq) for b, tg in zip(batches, tags) for seq, st in zip(b, tg)}
+    recompute = []
+
+    def sel(i, B, tables):
+        rng = np.random.default_rng(seed * 1000 + i)
+        pick = set(rng.choice(B, size=min(per_batch, B), replace=False).tolist())
+        for r, (sid, t) in enumerate(tags[i]):
+            if t > 0 and tables["prefix_lens"][r] < seqlen[(sid, t - 1)]:
+                pick.add(r)
+                recompute.append((i, r))
+        return sorted(pick)
+    return shape, phases, sel, recompute
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,per_batch", [("c5", 3), ("c5e", 2)])
+def test_extend_c5_chat(name, per_batch):
+    """Multi-turn chat through the whole cache: 89 batches of prepare, store,
+    extend and commit; c5e evicts under a 2^19-slot pool and recomputes."""
+    shape, phases, sel, recompute = chat_selector(name, per_batch)
+    res, _ = G.run(shape, phases, select=sel, sparse=True)
+    G.check(res, "bf16", name)
+    G.log(f"{name}: {sum(len(r['requests']) for r in res)} turns checked, "
+          f"{len(recompute) // 2} of them recompute evicted history")
+    if name == "c5e":
+        # the selector runs twice (slot dry run + the run itself)
+        assert len(recompute) // 2 == 32
+    else:
+        assert not recompute
+
+
 # ---------------------------------------------------------------- decode
 def decode_workload(shape, lengths, shared=300, seed=7):
     """Histories cached in a setup batch, then one decode batch whose
