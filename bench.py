@@ -123,6 +123,49 @@ class Phase:
             self.cache.decode(self.batch, self.q, self.o, self.lse)
 
 
+def gqa_halves(steps, warmup):
+    """Llama-70B-shaped GQA (c4: 64 q / 8 kv heads, D=128, bf16, a shared
+    2048-token prefix): the extend half (64 requests x 256 new tokens) and the
+    decode half (64 requests x 1 token), each kv_scatter + attention, timed
+    with HIP events on the launch stream; reported separately and summed."""
+    import torch
+    from inputs import configs
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name, idx in (("extend", 2), ("decode", 3)):
+        ph = Phase("c4-" + name, configs.c4, idx)
+        for _ in range(warmup):
+            ph.scatter()
+            ph.attend()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        sc, at = [], []
+        for _ in range(steps):
+            ev[0].record(stream); ph.scatter(); ev[1].record(stream); ph.attend(); ev[2].record(stream)
+            torch.cuda.synchronize()
+            sc.append(ev[0].elapsed_time(ev[1])); at.append(ev[1].elapsed_time(ev[2]))
+        tb, s_ = ph.batch.host, ph.shape
+        us, sus = float(np.mean(at)) * 1e3, float(np.mean(sc)) * 1e3
+        T = int(tb["qo_indptr"][-1])
+        if name == "extend":
+            F = extend_flops(tb["prefix_lens"], tb["seq_lens"], s_.hq, s_.d)
+            out[name] = dict(kernel="attn_extend", us=us, scatter_us=sus, flop=F, tflops=F / (us * 1e-6) / 1e12,
+                             frac_of_peak=F / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
+                             tokens_per_s=T / ((us + sus) * 1e-6))
+        else:
+            Bl = decode_bytes(tb["seq_lens"], s_.hq, s_.hkv, s_.d, 2)
+            out[name] = dict(kernel="attn_decode", us=us, scatter_us=sus, bytes_logical=Bl,
+                             gbs_logical=Bl / (us * 1e-6) / 1e9,
+                             frac_of_peak=Bl / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, tokens_per_s=T / ((us + sus) * 1e-6))
+        del ph
+        torch.cuda.empty_cache()
+    tot = out["extend"]["us"] + out["extend"]["scatter_us"] + out["decode"]["us"] + out["decode"]["scatter_us"]
+    out["summed"] = dict(us=tot, tokens=64 * 256 + 64, tokens_per_s=(64 * 256 + 64) / (tot * 1e-6))
+    out["workload"] = ("llama70b-gqa: 128 requests share a 2048-token prefix; 64 extend 256 tokens (contexts "
+                       "2304-8192), 64 decode 1 token (contexts 2049-8192); 64/8 heads, D=128, bf16, 2^20 slots")
+    return out
+
+
 def chat_pipeline(name):
     """Multi-turn chat replay (c5: 512 sessions, 89 batches; c5e: the same
     trace on a 2^19-slot pool, where LRU eviction and recompute bind), timed
@@ -403,6 +446,7 @@ def main():
     }
     del ext, dec
     torch.cuda.empty_cache()
+    out["gqa_llama70b"] = gqa_halves(max(5, args.steps // 2), 3)
     out["chat_pipeline"] = [chat_pipeline("c5"), chat_pipeline("c5e")]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
