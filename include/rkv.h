@@ -223,7 +223,7 @@ size_t rkv_attn_decode_workspace_bytes(int32_t B, int32_t hq, int32_t d, int32_t
  * extend).  Split-KV: the keys of a request are cut into S_r contiguous
  * chunks, each reduced to a partial (max, sum, acc) in fp32, then merged by
  * log-sum-exp rescaling.  S_r depends only on L_r and num_splits (0 = a
- * fixed chunk of 256 keys; N > 0 = at most N chunks), never on the rest of
+ * fixed chunk of 768 keys; N > 0 = at most N chunks), never on the rest of
  * the batch, so a request's output bits do not depend on its batch.  Every
  * seq_lens[r] must be <= max_seq_len and <= ld.  `workspace` (ws_bytes >=
  * rkv_attn_decode_workspace_bytes) holds the partials.

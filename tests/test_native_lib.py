@@ -47,5 +47,5 @@ def test_host_argument_errors():
     L = rkv.lib()
     assert L.rkv_attn_decode_workspace_bytes(4, 8, 96, 100, 0) == 0   # unsupported D
     # B * Hq * splits(1024 keys / 256 per split) * (D + 4) floats
-    assert L.rkv_attn_decode_workspace_bytes(4, 8, 128, 1024, 0) == 4 * 8 * 4 * 132 * 4
+    assert L.rkv_attn_decode_workspace_bytes(4, 8, 128, 1024, 0) == 4 * 8 * 2 * 132 * 4   # 768-key chunks
     assert L.rkv_attn_decode_workspace_bytes(4, 8, 128, 1024, 3) == 4 * 8 * 3 * 132 * 4
