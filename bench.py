@@ -223,6 +223,31 @@ def chat_pipeline(name):
     return out
 
 
+def queue_orders():
+    """Cache hit rate of the multi-turn chat trace under a serving queue (a
+    session's next turn is runnable once its previous turn ran; <= 64 turns a
+    step), first come first served vs cache-aware (rkv_schedule: longest
+    reusable prefix first), on the native tree; host only."""
+    from inputs import configs
+    from prefix_shared_kv_host_amd import rkv, serving
+    out = []
+    for name in ("c5", "c5e"):
+        s, _ = configs.build(name)
+        batches, tags = configs.chat_trace(s.seed)
+        turns = {st: seq for b, tg in zip(batches, tags) for seq, st in zip(b, tg)}
+        arrival = [st for tg in tags for st in tg]
+        row = dict(workload=f"{name}: 512 sessions, 2241 turns, pool 2^{int(np.log2(s.pool))} slots")
+        for policy in ("fcfs", "cache"):
+            tree = rkv.Tree(s.pool, configs.free_list(s.pool, s.seed))
+            t0 = time.perf_counter()
+            r = serving.run_queue(tree, turns, arrival, policy)
+            row[policy] = dict(hit_rate=r["hit_rate"], reused_tokens=r["reused_tokens"], steps=r["steps"],
+                               evicted_tokens=int(tree.stats()[7]), host_s=time.perf_counter() - t0)
+        row["prompt_tokens"] = r["prompt_tokens"]
+        out.append(row)
+    return out
+
+
 def time_host_radix(phase_obj, reps=3):
     """ns per token of batch_prepare + batch_commit on a fresh native tree
     replaying the same workload (host only)."""
@@ -448,6 +473,7 @@ def main():
     torch.cuda.empty_cache()
     out["gqa_llama70b"] = gqa_halves(max(5, args.steps // 2), 3)
     out["chat_pipeline"] = [chat_pipeline("c5"), chat_pipeline("c5e")]
+    out["cache_aware_scheduling"] = queue_orders()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out))

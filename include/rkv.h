@@ -91,6 +91,22 @@ void rkv_tree_destroy(rkv_tree* t);
 int rkv_radix_match(rkv_tree* t, const int32_t* tok, int64_t n, int32_t* out_slots,
                     int64_t* out_len, int64_t* out_node);
 
+/* Length of the longest cached prefix of tok[0..n), with no side effect on
+ * the tree: no split, no LRU stamp, no lock (a read-only rkv_radix_match, for
+ * schedulers that rank waiting requests).  *out_len = that length. */
+int rkv_radix_peek(const rkv_tree* t, const int32_t* tok, int64_t n, int64_t* out_len);
+
+/* Cache-aware order of a waiting queue (unite.ai, "SGLang: Efficient
+ * Execution of Structured Language Model Programs", section "SGLang:
+ * Evaluacion y resultados": cache-aware scheduling keeps hit rates close to
+ * the optimum).  Request q is tok[tok_indptr[q] .. tok_indptr[q+1]) (int64
+ * offsets, Q+1 of them).  matched[q] = the prefix a batch would reuse now:
+ * rkv_radix_peek of its first L_q - 1 tokens (0 for an empty request).
+ * order[0..Q) = queue positions by matched descending, ties in queue order
+ * (stable).  Read-only on the tree.  Q = 0 is a no-op. */
+int rkv_schedule(const rkv_tree* t, int32_t Q, const int32_t* tok, const int64_t* tok_indptr,
+                 int32_t* order, int64_t* matched);
+
 /* lock: +1 on the lock count of `node` and every ancestor up to, not
  * including, the root; locked nodes are never evicted.  unlock: -1 on the
  * same nodes; EINVAL (and no change) if any count would go negative or the

@@ -121,6 +121,35 @@ class OracleTree:
         return node, m, slots, path
 
     # ------------------------------------------------------------------ core ops
+    def peek(self, tok):
+        """Length of the longest cached prefix of tok, leaving the tree
+        untouched (no split, no tick): what a scheduler ranks requests by."""
+        tok = [int(t) for t in tok]
+        node, m = self.root, 0
+        while m < len(tok):
+            c = self._child(node, tok[m])
+            if c is None:
+                break
+            k = 0
+            while k < len(c.label) and m + k < len(tok) and c.label[k] == tok[m + k]:
+                k += 1
+            m += k
+            if k < len(c.label):
+                break
+            node = c
+        return m
+
+    def schedule(self, seqs):
+        """Cache-aware order of a waiting queue (the article, section "SGLang:
+        Evaluacion y resultados": cache-aware scheduling approaches the optimal
+        hit rate; its rule is not given).  Reading: rank by the prefix a batch
+        would reuse now (peek of the first L-1 tokens, as batch_prepare caps
+        its match), longest first, ties in queue order.  Returns (order,
+        matched)."""
+        matched = [self.peek(list(s)[: len(s) - 1]) if len(s) > 0 else 0 for s in seqs]
+        order = sorted(range(len(seqs)), key=lambda q: (-matched[q], q))
+        return order, matched
+
     def match(self, tok):
         """Longest cached prefix of tok: (matched length, slots, stop node id)."""
         tok = [int(t) for t in tok]

@@ -173,6 +173,28 @@ struct rkv_tree {
     return node;
   }
 
+  // Length of the longest cached prefix of tok[0..n), with no side effect:
+  // no split, no tick, no lock (the walk stops inside an edge instead of
+  // cutting it).
+  int64_t peek(const int32_t* tok, int64_t n) const {
+    const Node* node = &root;
+    int64_t m = 0;
+    while (m < n) {
+      auto it = std::lower_bound(node->kids.begin(), node->kids.end(), tok[m],
+                                 [](const std::pair<int32_t, Node*>& a, int32_t b) { return a.first < b; });
+      if (it == node->kids.end() || it->first != tok[m]) break;
+      const Node* c = it->second;
+      const int64_t lab = (int64_t)c->label.size();
+      const int64_t lim = std::min<int64_t>(lab, n - m);
+      int64_t k = 1;
+      while (k < lim && c->label[k] == tok[m + k]) ++k;
+      m += k;
+      if (k < lab) break;
+      node = c;
+    }
+    return m;
+  }
+
   int64_t do_match(const int32_t* tok, int64_t n, int32_t* slots, int64_t* node_id) {
     ++tick;
     int64_t m = 0;
@@ -307,6 +329,31 @@ int rkv_radix_match(rkv_tree* t, const int32_t* tok, int64_t n, int32_t* out_slo
   if (!t || !out_len || !out_node || n < 0 || (n > 0 && (!tok || !out_slots)))
     return bad("rkv_radix_match: bad argument");
   *out_len = t->do_match(tok, n, out_slots, out_node);
+  return RKV_OK;
+}
+
+int rkv_radix_peek(const rkv_tree* t, const int32_t* tok, int64_t n, int64_t* out_len) {
+  rkv::clear_error();
+  if (!t || !out_len || n < 0 || (n > 0 && !tok)) return bad("rkv_radix_peek: bad argument");
+  *out_len = t->peek(tok, n);
+  return RKV_OK;
+}
+
+int rkv_schedule(const rkv_tree* t, int32_t Q, const int32_t* tok, const int64_t* tok_indptr,
+                 int32_t* order, int64_t* matched) {
+  rkv::clear_error();
+  if (!t || Q < 0) return bad("rkv_schedule: bad argument");
+  if (Q == 0) return RKV_OK;
+  if (!tok_indptr || !order || !matched) return bad("rkv_schedule: NULL pointer");
+  for (int32_t q = 0; q < Q; ++q) {
+    const int64_t L = tok_indptr[q + 1] - tok_indptr[q];
+    if (L < 0 || tok_indptr[q] < 0) return bad("rkv_schedule: tok_indptr must be non-decreasing from 0");
+    if (L > 0 && !tok) return bad("rkv_schedule: tok is NULL");
+    // the cached part a batch would reuse: prepare caps the match at L - 1
+    matched[q] = L > 0 ? t->peek(tok + tok_indptr[q], L - 1) : 0;
+    order[q] = q;
+  }
+  std::stable_sort(order, order + Q, [&](int32_t x, int32_t y) { return matched[x] > matched[y]; });
   return RKV_OK;
 }
 

@@ -29,7 +29,7 @@ EXPORTS = (
     "rkv_radix_lock", "rkv_radix_unlock", "rkv_radix_insert", "rkv_radix_evict", "rkv_alloc",
     "rkv_free", "rkv_stats", "rkv_radix_serialize", "rkv_free_list", "rkv_batch_prepare",
     "rkv_batch_commit", "rkv_kv_scatter", "rkv_attn_extend", "rkv_attn_decode_workspace_bytes",
-    "rkv_attn_decode",
+    "rkv_attn_decode", "rkv_radix_peek", "rkv_schedule",
 )
 
 
@@ -61,6 +61,8 @@ def lib():
         "rkv_tree_create": (ctypes.c_int, [ctypes.POINTER(_vp), _i64, c_i32p]),
         "rkv_tree_destroy": (None, [_vp]),
         "rkv_radix_match": (ctypes.c_int, [_vp, c_i32p, _i64, c_i32p, c_i64p, c_i64p]),
+        "rkv_radix_peek": (ctypes.c_int, [_vp, c_i32p, _i64, c_i64p]),
+        "rkv_schedule": (ctypes.c_int, [_vp, _i32, c_i32p, c_i64p, c_i32p, c_i64p]),
         "rkv_radix_lock": (ctypes.c_int, [_vp, _i64]),
         "rkv_radix_unlock": (ctypes.c_int, [_vp, _i64]),
         "rkv_radix_insert": (ctypes.c_int, [_vp, c_i32p, c_i32p, _i64, c_i64p]),
@@ -138,6 +140,25 @@ class Tree:
         _check(lib().rkv_radix_match(self._h, p, a.shape[0], out.ctypes.data_as(c_i32p),
                                      ctypes.byref(m), ctypes.byref(node)))
         return m.value, out[: m.value].tolist(), node.value
+
+    def radix_peek(self, tok) -> int:
+        """Longest cached prefix length of tok, with no side effect on the tree."""
+        a, p = _i32arr(tok)
+        m = _i64()
+        _check(lib().rkv_radix_peek(self._h, p, a.shape[0], ctypes.byref(m)))
+        return m.value
+
+    def schedule(self, seqs):
+        """Cache-aware order of a waiting queue: (order, matched) as NumPy
+        arrays; order = queue positions by matched prefix, longest first, ties
+        in queue order."""
+        Q = len(seqs)
+        flat, indptr, _ = self._flat(seqs)
+        order = np.empty(max(Q, 1), dtype=np.int32)
+        matched = np.empty(max(Q, 1), dtype=np.int64)
+        _check(lib().rkv_schedule(self._h, Q, flat.ctypes.data_as(c_i32p), indptr.ctypes.data_as(c_i64p),
+                                  order.ctypes.data_as(c_i32p), matched.ctypes.data_as(c_i64p)))
+        return order[:Q], matched[:Q]
 
     def radix_lock(self, node) -> int:
         return lib().rkv_radix_lock(self._h, int(node))
