@@ -79,9 +79,11 @@ int main(int argc, char** argv) {
     for (auto& x : tok) x = (int32_t)(rng() % (uint64_t)vocab);
     if (kind < 25) {
       std::vector<int32_t> out((size_t)L);
-      int64_t m = 0, node = 0;
+      int64_t m = 0, node = 0, peeked = -1;
+      CHECK(rkv_radix_peek(t, tok.data(), L, &peeked) == RKV_OK);
       CHECK(rkv_radix_match(t, tok.data(), L, out.data(), &m, &node) == RKV_OK);
       CHECK(m >= 0 && m <= L);
+      CHECK(peeked == m);   // the read-only walk finds what the match finds
       if (node != 0 && (rng() & 1)) {
         CHECK(rkv_radix_lock(t, node) == RKV_OK);
         locked_nodes.push_back(node);
@@ -137,11 +139,15 @@ int main(int argc, char** argv) {
       std::vector<int32_t> r2t((size_t)(B * ld)), pl((size_t)B), sl((size_t)B), qo((size_t)B + 1),
           ns(flat.size());
       std::vector<int64_t> nodes((size_t)B);
+      // the schedule's reusable prefixes are what prepare then matches
+      std::vector<int32_t> order((size_t)B);
+      std::vector<int64_t> reuse((size_t)B);
+      CHECK(rkv_schedule(t, B, flat.data(), indptr.data(), order.data(), reuse.data()) == RKV_OK);
       const int rc = rkv_batch_prepare(t, B, flat.data(), indptr.data(), r2t.data(), ld, pl.data(), sl.data(),
                                        qo.data(), ns.data(), (int64_t)flat.size(), nodes.data());
       CHECK(rc == RKV_OK || rc == RKV_EBUSY);
       if (rc == RKV_OK) {
-        for (int r = 0; r < B; ++r) CHECK(pl[(size_t)r] < sl[(size_t)r]);
+        for (int r = 0; r < B; ++r) CHECK(pl[(size_t)r] < sl[(size_t)r] && pl[(size_t)r] == reuse[(size_t)r]);
         CHECK(rkv_batch_commit(t, B, flat.data(), indptr.data(), r2t.data(), ld, nodes.data()) == RKV_OK);
       }
     }
