@@ -253,6 +253,74 @@ int rkv_attn_decode(const void* q, const void* k_pool, const void* v_pool, void*
                     float sm_scale, int32_t dtype, int32_t num_splits, void* workspace,
                     size_t ws_bytes, int64_t pool_slots, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Prefix-shared ("cascade") decode.  Requests under one radix node gather the
+ * same slots for that node's keys (the page's RadixAttention bullet, section
+ * "Introduccion a SGLang": a shared prefix is cached once and reused).  This
+ * extension reads each such shared run once per decode batch for all of its
+ * requests and merges the partial softmax state with each request's private
+ * remainder, by the same log-sum-exp rule as split-KV decode.  The result is
+ * the decode attention defined above; only the rounding order differs.
+ * ------------------------------------------------------------------------ */
+
+/* Host planner.  From the host copy of a decode batch's table
+ * (req_to_token [B, ld], seq_lens[B], 1 <= L_r <= ld) it finds the runs of
+ * keys that several requests share with identical slots:
+ *   - row r is considered over its first L_r - 1 keys (the query key is
+ *     private); perm[0..B) = requests sorted by that row (slot ids compared
+ *     as int32 sequences, a proper prefix first), ties by request id;
+ *   - every maximal block of requests sharing a prefix deeper than their
+ *     parent block's gives a segment [start, depth), where start is the end
+ *     of the last emitted segment above it; a segment shorter than min_keys
+ *     is not emitted and its keys fall to the segments (or tails) below;
+ *   - segments are cut into seg_chunk-key chunks and into member groups of
+ *     at most max_members (consecutive in perm).  jobs[5*i ..] =
+ *     {key_begin, key_end, first, count, rec_off}: the requests
+ *     perm[first .. first+count) share slots over [key_begin, key_end) of
+ *     their rows; each gets that chunk's partial in its record rec_off;
+ *   - tail_begin[r]: first key of r's private tail (always < L_r); the tail
+ *     is cut into tail_chunk-key splits;
+ *   - records of r: its shared chunks in path order, then its tail splits;
+ *     rec_indptr[B+1] = their prefix sums (rec_indptr[B] = n_records);
+ *     *out_tail_splits = the most tail splits of any request.
+ * Jobs are in a preorder of the prefix tree.  jobs_cap counts jobs (5 int32
+ * each); with fewer than needed the call returns RKV_ENOSPC, sets
+ * *out_n_jobs to the number needed and writes nothing else (call with
+ * jobs_cap 0 and jobs NULL to size).  EINVAL on bad sizes or NULL pointers.
+ * O(sum L_r log B) time. */
+int rkv_cascade_plan(const int32_t* req_to_token, int64_t ld, const int32_t* seq_lens, int32_t B,
+                     int32_t seg_chunk, int32_t tail_chunk, int32_t min_keys, int32_t max_members,
+                     int32_t* perm, int32_t* rec_indptr, int32_t* tail_begin, int32_t* jobs,
+                     int64_t jobs_cap, int64_t* out_n_jobs, int32_t* out_tail_splits);
+
+/* Bytes of device workspace rkv_attn_decode_cascade needs: n_records
+ * records of Hq rows of (d + 4) fp32.  0 on bad arguments. */
+size_t rkv_attn_decode_cascade_workspace_bytes(int64_t n_records, int32_t hq, int32_t d);
+
+/* Decode (same inputs, outputs and formula as rkv_attn_decode) following a
+ * plan from rkv_cascade_plan built on the same req_to_token and seq_lens,
+ * with the same max_members and tail_chunk; perm, rec_indptr, tail_begin
+ * and jobs are that plan's arrays copied to the device, n_jobs, tail_splits
+ * and n_records (= rec_indptr[B]) its host values.  Phase 1 runs one wave
+ * per (kv head, job): the job's keys are gathered once, from the row of
+ * request perm[first], for the count * (Hq/Hkv) query columns of its
+ * members (bf16 MFMA; max_members * Hq/Hkv columns at most 32 for d = 128
+ * and 64 for d = 64, ENOTSUP otherwise), and one wave or workgroup per (request, tail split)
+ * covers the private keys; phase 2 merges each request's records.  bf16
+ * only (ENOTSUP otherwise); arithmetic as in rkv_attn_decode's MFMA path.
+ * The plan's values are checked in the kernels before they index anything:
+ * a job or request that does not fit is skipped, and with RKV_DEBUG=1 the
+ * call returns RKV_EINVAL.  Workspace: rkv_attn_decode_cascade_workspace_bytes
+ * (may be NULL when n_jobs == 0 and n_records == B: every request then has
+ * one partial). */
+int rkv_attn_decode_cascade(const void* q, const void* k_pool, const void* v_pool, void* o, float* lse,
+                            const int32_t* req_to_token, int64_t ld, const int32_t* seq_lens, int32_t B,
+                            int32_t max_seq_len, int32_t hq, int32_t hkv, int32_t d, float sm_scale,
+                            int32_t dtype, const int32_t* perm, const int32_t* rec_indptr,
+                            const int32_t* tail_begin, const int32_t* jobs, int64_t n_jobs,
+                            int32_t max_members, int32_t tail_chunk, int32_t tail_splits, int64_t n_records,
+                            void* workspace, size_t ws_bytes, int64_t pool_slots, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

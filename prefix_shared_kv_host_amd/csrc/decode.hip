@@ -27,6 +27,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <string>
+
 #include "device.h"
 #include "rkv.h"
 #include "rkv_internal.h"
@@ -55,12 +57,71 @@ struct DecodeArgs {
   int64_t pool_slots;
   float* ws;                      // [B, hq, splits, D + 4]: acc[D], max, sum, pad
   int* err;
+  // prefix-shared plan (all null for plain decode): the partials of request
+  // r are records rec_indptr[r] .. rec_indptr[r+1] of ws, laid out
+  // [record, hq, D + 4]; its private keys tail_begin[r] .. L_r are cut into
+  // tail_chunk-key splits that fill the last records of that range
+  const int32_t* rec_indptr;
+  const int32_t* tail_begin;
+  int32_t n_records;
+  int32_t tail_chunk;
+};
+
+// Prefix-shared jobs: keys [key_begin, key_end) of request perm[first]'s row
+// are common to the `count` requests perm[first .. first+count); each of them
+// gets that range's partial in its record rec_indptr[r] + rec_off.
+struct SharedJobs {
+  const int32_t* jobs;            // [n_jobs, 5]: key_begin, key_end, first, count, rec_off
+  const int32_t* perm;            // [B]
+  int32_t n_jobs;
+  int32_t max_members;
 };
 
 __host__ __device__ inline int split_chunk(int L, int num_splits) {
   if (num_splits <= 0) return kChunk;
   int c = (L + num_splits - 1) / num_splits;
   return ((c + 63) / 64) * 64;
+}
+
+// Keys [k_begin, k_end) of split s of request r (of length L), and where its
+// partial goes: rec < 0 means the split is the request's only partial and
+// writes o and lse itself; otherwise the partial goes to workspace record
+// `rec` (plain layout: split index; prefix-shared layout: record index).
+// Returns false when the split is empty, or when a prefix-shared plan does
+// not fit the request (flag raised in debug mode; nothing is written).
+__device__ __forceinline__ bool split_span(const DecodeArgs& a, int r, int s, int L, int& k_begin, int& k_end,
+                                           int& rec, int& nsplit) {
+  if (!a.rec_indptr) {
+    const int chunk = split_chunk(L, a.num_splits);
+    nsplit = (L + chunk - 1) / chunk;
+    if (s >= nsplit) return false;
+    k_begin = s * chunk;
+    k_end = min(L, k_begin + chunk);
+    rec = nsplit == 1 ? -1 : s;
+    return true;
+  }
+  const int tb = a.tail_begin[r];
+  const int r0 = a.rec_indptr[r], r1 = a.rec_indptr[r + 1];
+  nsplit = (L - tb + a.tail_chunk - 1) / a.tail_chunk;
+  if (tb < 0 || tb >= L || r0 < 0 || r1 > a.n_records || r1 - r0 < nsplit) {
+    if (s == 0 && a.err) rkv::raise_flag(a.err);
+    return false;
+  }
+  if (s >= nsplit) return false;
+  k_begin = tb + s * a.tail_chunk;
+  k_end = min(L, k_begin + a.tail_chunk);
+  rec = (r1 - r0 == 1) ? -1 : r1 - nsplit + s;
+  if (rec >= 0 && !a.ws) {
+    if (a.err) rkv::raise_flag(a.err);
+    return false;
+  }
+  return true;
+}
+
+// Workspace row of (request r, q head, record/split rec).
+__device__ __forceinline__ float* ws_row(const DecodeArgs& a, int D, int r, int head, int rec) {
+  if (a.rec_indptr) return a.ws + ((int64_t)rec * a.hq + head) * (D + 4);
+  return a.ws + (((int64_t)r * a.hq + head) * a.splits + rec) * (D + 4);
 }
 
 template <typename T>
@@ -128,11 +189,8 @@ __global__ __launch_bounds__(256) void decode_partial(DecodeArgs a) {
   const int hblk = (int)(rest / a.hg);
   if (hblk * HB >= a.hkv) return;
   const int L = min(a.seq_lens[r], a.max_seq_len);
-  const int chunk = split_chunk(L, a.num_splits);
-  const int nsplit = (L + chunk - 1) / chunk;
-  if (s >= nsplit) return;
-  const int k_begin = s * chunk;
-  const int k_end = min(L, k_begin + chunk);
+  int k_begin, k_end, rec, nsplit;
+  if (!split_span(a, r, s, L, k_begin, k_end, rec, nsplit)) return;
   const int h0 = sub * kMaxG;                   // first q head of this group within a kv group
   const int nh = min(G, a.G - h0);              // q heads handled here (<= G)
 
@@ -268,14 +326,14 @@ __global__ __launch_bounds__(256) void decode_partial(DecodeArgs a) {
   for (int hh = 0; hh < G; ++hh) {
     if (hh >= nh) break;
     const int head = g * a.G + h0 + hh;
-    if (nsplit == 1) {
+    if (rec < 0) {
       const float inv = 1.f / l[hh];
       const int64_t ooff = ((int64_t)r * a.hq + head) * D + lr * VEC;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) E::store1(a.o, ooff + e, acc[hh][e] * inv);
       if (a.lse && lr == 0) a.lse[(int64_t)r * a.hq + head] = (m[hh] + log2f(l[hh])) * 0.69314718055994531f;
     } else {
-      float* dst = a.ws + (((int64_t)r * a.hq + head) * a.splits + s) * (D + 4);
+      float* dst = ws_row(a, D, r, head, rec);
 #pragma unroll
       for (int e = 0; e < VEC; ++e) dst[lr * VEC + e] = acc[hh][e];
       if (lr == 0) {
@@ -286,11 +344,15 @@ __global__ __launch_bounds__(256) void decode_partial(DecodeArgs a) {
   }
 }
 
-// Phase 1 for grouped heads (bf16, Hq/Hkv >= 4): the G query heads of a kv
-// head share every K/V row, so the scores are a small matrix product.  One
-// wave per (request, kv head, split) puts the G heads in the N dimension of
-// v_mfma_f32_16x16x32_bf16 (S^T = K Q^T, 16 keys x 16 head columns, G of
-// them used) and walks the split 32 keys at a time:
+// Phase 1 on the matrix cores (bf16): query columns that read the same K/V
+// rows go through v_mfma_f32_16x16x32_bf16 together as the N dimension
+// (S^T = K Q^T, 16 keys x 16 query columns per block).  Two users:
+//   * grouped heads (Hq/Hkv >= 4): one wave per (request, kv head, split),
+//     the G query heads of the kv head are the columns (one block);
+//   * prefix-shared jobs: one wave per (job, kv head); the columns are
+//     (member request, q head) pairs, up to CB blocks of 16, and every block
+//     reuses the same K operands and the same V tile.
+// One wave walks its keys 32 at a time:
 //   * each lane gathers the 16-byte pieces of its two K rows straight into
 //     MFMA A operands (registers, one step ahead);
 //   * the 32 V rows are copied global -> LDS by 16-byte DMA (two stages) and
@@ -298,8 +360,8 @@ __global__ __launch_bounds__(256) void decode_partial(DecodeArgs a) {
 //   * K rows are assigned so that a lane's S^T accumulators hold 8 consecutive
 //     keys, which is its slice of the bf16 P^T operand;
 //   * fp32 online softmax in the log2 domain, row sums on the MFMA.
-// Memory traffic is the same as the other phase-1 kernel; the arithmetic moves
-// from VALU FMAs (8 per head per element) to the matrix cores.
+// Memory traffic is the same as the vector kernel's for one block; the
+// arithmetic moves from VALU FMAs (8 per head per element) to the matrix cores.
 namespace gqa {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -312,11 +374,25 @@ template <int CH>
 __device__ __forceinline__ int swz_v(int row) {
   return CH == 16 ? ((row & 3) | (((row >> 3) & 3) << 2)) : ((row & 3) | (((row >> 3) & 1) << 2));
 }
-}  // namespace gqa
 
-template <int D>
-__global__ __launch_bounds__(64) void decode_gqa(DecodeArgs a) {
-  using namespace gqa;
+// Online-softmax state of CB column blocks; lane (column l16, group gq)
+// holds o for d = db*16 + 4*gq + [0..3], the row sum in l[cb][0], and the
+// running maximum (log2 domain) of its column in m[cb].
+template <int D, int CB>
+struct State {
+  f32x4 o[CB][D / 16];
+  f32x4 l[CB];
+  float m[CB];
+};
+
+// Walks keys [k_begin, k_end) of row_tab for kv head g; q[cb][k] is the Q^T
+// operand of block cb (columns l16, rows d = k*32 + 8*gq + [0..7]).  Blocks
+// cb >= ncb (wave-uniform) are skipped.  Every gather is clamped into the
+// range and into the pool.
+template <int D, int CB>
+__device__ __forceinline__ void walk(const DecodeArgs& a, const int32_t* row_tab, int k_begin, int k_end, int g,
+                                     const bf16x8 (&q)[CB][D / 32], int ncb, State<D, CB>& st,
+                                     char (&Vs)[2][32 * D * 2]) {
   constexpr int ROWB = D * 2;
   constexpr int CH = D / 8;
   constexpr int KSTEPS = D / 32;
@@ -324,53 +400,16 @@ __global__ __launch_bounds__(64) void decode_gqa(DecodeArgs a) {
   constexpr int STEP = 32;
   constexpr int RPI = 1024 / ROWB;          // V rows per DMA instruction
   constexpr int NDMA = STEP / RPI;          // DMA instructions per step
-  __shared__ __attribute__((aligned(16))) char Vs[2][STEP * ROWB];
-
-  const int64_t w = rkv::xcd_work_item(blockIdx.x, gridDim.x);
-  const int s = (int)(w % a.splits);
-  int64_t rest = w / a.splits;
-  const int r = (int)(rest % a.B);
-  const int g = (int)(rest / a.B);
-  if (g >= a.hkv) return;
-  const int L = min(a.seq_lens[r], a.max_seq_len);
-  const int chunk = split_chunk(L, a.num_splits);
-  const int nsplit = (L + chunk - 1) / chunk;
-  if (s >= nsplit) return;
-  const int k_begin = s * chunk;
-  const int k_end = min(L, k_begin + chunk);
-
   const int lane = threadIdx.x;
   const int l16 = lane & 15, gq = lane >> 4;
-  const int G = a.G;
-  const bool hvalid = l16 < G;
-  const int head = g * G + (hvalid ? l16 : 0);
-
-  // Q^T operand: column l16 = query head, rows d = s*32 + 8*gq + [0..7]
-  bf16x8 qreg[KSTEPS];
-  {
-    const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)r * a.hq + head) * D + gq * 8;
-#pragma unroll
-    for (int k = 0; k < KSTEPS; ++k) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (hvalid) v = *(const uint4*)(qp + k * 32);
-      qreg[k] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
-  f32x4 oacc[DBLK];
-#pragma unroll
-  for (int db = 0; db < DBLK; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 lacc = f32x4{0.f, 0.f, 0.f, 0.f};
-  float mref = -INFINITY;
   const float c = a.scale_log2e;
   const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
 
-  const int32_t* row_tab = a.r2t + (int64_t)r * a.ld;
   const uint32_t P = (uint32_t)min(a.pool_slots, (int64_t)0x7fffffff);
   const uint32_t slot_bytes = (uint32_t)a.hkv * ROWB;
   const char* kg = (const char*)a.kp + (uint64_t)g * ROWB + gq * 16;
   const char* vg = (const char*)a.vp + (uint64_t)g * ROWB;
-  // lane (lane & 31) holds the slot of key base + (lane & 31); clamped into
-  // the split and into the pool, so every gather stays in bounds
+  // lane (lane & 31) holds the slot of key base + (lane & 31)
   auto fetch = [&](int base) -> int32_t {
     int32_t slot = row_tab[min(base + (lane & 31), k_end - 1)];
     if ((uint32_t)slot >= P) {
@@ -418,43 +457,49 @@ __global__ __launch_bounds__(64) void decode_gqa(DecodeArgs a) {
       load_k(slots);
       dma_v(slots, stage ^ 1);
     }
-    f32x4 sacc[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k = 0; k < KSTEPS; ++k)
-        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb][k], qreg[k], sacc[kb], 0, 0, 0);
-    }
-    // lane (head l16, group gq) holds keys base + 8*gq + 4*kb + i
+    // lane (column l16, group gq) holds keys base + 8*gq + 4*kb + i
     const int lim = k_end - 1 - base - 8 * gq;
+    bf16x8 pb[CB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int cb = 0; cb < CB; ++cb) {
+      if (cb >= ncb) break;
+      f32x4 sacc[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (4 * kb + i > lim) sacc[kb][i] = -INFINITY;
-    float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
-                     fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
-    mx = rkv::max_xor16(mx);
-    mx = rkv::max_xor32(mx);
-    const float mt = mx * c;
-    if (__builtin_amdgcn_ballot_w64(mt > mref + kRescaleThreshold)) {
-      const float mn = fmaxf(mref, mt);
-      const float alpha = __builtin_amdgcn_exp2f(mref - mn);
-      mref = mn;
-      lacc *= alpha;
+      for (int kb = 0; kb < 2; ++kb) {
+        sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int db = 0; db < DBLK; ++db) oacc[db] *= alpha;
+        for (int k = 0; k < KSTEPS; ++k)
+          sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb][k], q[cb][k], sacc[kb], 0, 0, 0);
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (4 * kb + i > lim) sacc[kb][i] = -INFINITY;
+      float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
+                       fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
+      mx = rkv::max_xor16(mx);
+      mx = rkv::max_xor32(mx);
+      const float mt = mx * c;
+      if (__builtin_amdgcn_ballot_w64(mt > st.m[cb] + kRescaleThreshold)) {
+        const float mn = fmaxf(st.m[cb], mt);
+        const float alpha = __builtin_amdgcn_exp2f(st.m[cb] - mn);
+        st.m[cb] = mn;
+        st.l[cb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) st.o[cb][db] *= alpha;
+      }
+      uint32_t wv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int kb = e >> 1, i = 2 * (e & 1);
+        wv[e] = rkv::pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c, -st.m[cb])),
+                                 __builtin_amdgcn_exp2f(fmaf(sacc[kb][i + 1], c, -st.m[cb])));
+      }
+      pb[cb] = __builtin_bit_cast(bf16x8, make_uint4(wv[0], wv[1], wv[2], wv[3]));
+      st.l[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[cb], st.l[cb], 0, 0, 0);
     }
-    uint32_t wv[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int kb = e >> 1, i = 2 * (e & 1);
-      wv[e] = rkv::pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c, -mref)),
-                               __builtin_amdgcn_exp2f(fmaf(sacc[kb][i + 1], c, -mref)));
-    }
-    const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(wv[0], wv[1], wv[2], wv[3]));
-    lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb, lacc, 0, 0, 0);
+    // PV: one V^T operand of this tile at a time, reused by every block
     const char* vs = Vs[stage];
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) {
@@ -469,30 +514,152 @@ __global__ __launch_bounds__(64) void decode_gqa(DecodeArgs a) {
       const bf16x8 va = __builtin_bit_cast(
           bf16x8, make_uint4(__builtin_bit_cast(uint2, part[0]).x, __builtin_bit_cast(uint2, part[0]).y,
                              __builtin_bit_cast(uint2, part[1]).x, __builtin_bit_cast(uint2, part[1]).y));
-      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, oacc[db], 0, 0, 0);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        if (cb >= ncb) break;
+        st.o[cb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[cb], st.o[cb][db], 0, 0, 0);
+      }
     }
     stage ^= 1;
   }
   __builtin_amdgcn_s_waitcnt(0);
+}
+
+// Loads the Q^T operand of one column (zeros when the column is unused).
+template <int D>
+__device__ __forceinline__ void load_q(const void* qbase, int64_t row, bool valid, bf16x8 (&out)[D / 32]) {
+  const uint16_t* qp = (const uint16_t*)qbase + row * D + (threadIdx.x >> 4) * 8;
+#pragma unroll
+  for (int k = 0; k < D / 32; ++k) {
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (valid) v = *(const uint4*)(qp + k * 32);
+    out[k] = __builtin_bit_cast(bf16x8, v);
+  }
+}
+
+// Writes one column's unnormalised partial (o, max, sum) to a workspace row.
+template <int D>
+__device__ __forceinline__ void store_partial(float* dst, const f32x4 (&o)[D / 16], float m, float l) {
+  const int gq = threadIdx.x >> 4;
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) *(f32x4*)(dst + db * 16 + 4 * gq) = o[db];
+  if (gq == 0) {
+    dst[D] = m;
+    dst[D + 1] = l;
+  }
+}
+}  // namespace gqa
+
+template <int D>
+__global__ __launch_bounds__(64) void decode_gqa(DecodeArgs a) {
+  using namespace gqa;
+  __shared__ __attribute__((aligned(16))) char Vs[2][32 * D * 2];
+
+  const int64_t w = rkv::xcd_work_item(blockIdx.x, gridDim.x);
+  const int s = (int)(w % a.splits);
+  int64_t rest = w / a.splits;
+  const int r = (int)(rest % a.B);
+  const int g = (int)(rest / a.B);
+  if (g >= a.hkv) return;
+  const int L = min(a.seq_lens[r], a.max_seq_len);
+  int k_begin, k_end, rec, nsplit;
+  if (!split_span(a, r, s, L, k_begin, k_end, rec, nsplit)) return;
+
+  const int lane = threadIdx.x;
+  const int l16 = lane & 15, gq = lane >> 4;
+  const bool hvalid = l16 < a.G;
+  const int head = g * a.G + (hvalid ? l16 : 0);
+  bf16x8 qreg[1][D / 32];
+  load_q<D>(a.q, (int64_t)r * a.hq + head, hvalid, qreg[0]);
+  State<D, 1> st;
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) st.o[0][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.l[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m[0] = -INFINITY;
+  walk<D, 1>(a, a.r2t + (int64_t)r * a.ld, k_begin, k_end, g, qreg, 1, st, Vs);
   if (!hvalid) return;
-  // lane (head l16, group gq) holds d = db*16 + 4*gq + [0..3]
-  const float lsum = lacc[0];
-  if (nsplit == 1) {
+  const float lsum = st.l[0][0];
+  if (rec < 0) {
     const float inv = 1.f / lsum;
     uint16_t* orow = (uint16_t*)a.o + ((int64_t)r * a.hq + head) * D;
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db)
-      *(uint2*)(orow + db * 16 + 4 * gq) = make_uint2(rkv::pack_bf16x2(oacc[db][0] * inv, oacc[db][1] * inv),
-                                                      rkv::pack_bf16x2(oacc[db][2] * inv, oacc[db][3] * inv));
-    if (a.lse && gq == 0) a.lse[(int64_t)r * a.hq + head] = (mref + log2f(lsum)) * 0.69314718055994531f;
+    for (int db = 0; db < D / 16; ++db)
+      *(uint2*)(orow + db * 16 + 4 * gq) = make_uint2(rkv::pack_bf16x2(st.o[0][db][0] * inv, st.o[0][db][1] * inv),
+                                                      rkv::pack_bf16x2(st.o[0][db][2] * inv, st.o[0][db][3] * inv));
+    if (a.lse && gq == 0) a.lse[(int64_t)r * a.hq + head] = (st.m[0] + log2f(lsum)) * 0.69314718055994531f;
   } else {
-    float* dst = a.ws + (((int64_t)r * a.hq + head) * a.splits + s) * (D + 4);
+    store_partial<D>(ws_row(a, D, r, head, rec), st.o[0], st.m[0], lsum);
+  }
+}
+
+// Prefix-shared phase 1: one wave per (kv head, job), kv head outermost so
+// that the member groups of one chunk (consecutive jobs, same K/V) run side
+// by side on one XCD.  Column c = cb*16 + l16 is member c / G of the job and
+// q head g*G + c % G.  The plan's values are checked against the batch
+// before use; a job that does not fit is skipped (flag raised in debug mode).
+// Two waves per SIMD: the register budget of 256 per lane holds CB = 2 at
+// D = 128 (without the hint the compiler takes more and runs one wave).
+template <int D, int CB>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_shared(DecodeArgs a, SharedJobs j) {
+  using namespace gqa;
+  __shared__ __attribute__((aligned(16))) char Vs[2][32 * D * 2];
+
+  const int64_t w = rkv::xcd_work_item(blockIdx.x, gridDim.x);
+  const int job = (int)(w % j.n_jobs);
+  const int g = (int)(w / j.n_jobs);
+  if (g >= a.hkv) return;
+  const int32_t* jp = j.jobs + (int64_t)job * 5;
+  const int kb = jp[0], ke = jp[1], first = jp[2], count = jp[3], rec_off = jp[4];
+  if (kb < 0 || ke <= kb || ke > a.ld || first < 0 || count < 1 || count > j.max_members ||
+      first + count > a.B || rec_off < 0) {
+    if (g == 0 && a.err) rkv::raise_flag(a.err);
+    return;
+  }
+  const int rep = j.perm[first];
+  if ((unsigned)rep >= (unsigned)a.B) {
+    if (g == 0 && a.err) rkv::raise_flag(a.err);
+    return;
+  }
+  const int lane = threadIdx.x;
+  const int l16 = lane & 15;
+  const int ncb = (count * a.G + 15) / 16;
+  bf16x8 qreg[CB][D / 32];
+  int req[CB], head[CB];
+  bool valid[CB];
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db) *(f32x4*)(dst + db * 16 + 4 * gq) = oacc[db];
-    if (gq == 0) {
-      dst[D] = mref;
-      dst[D + 1] = lsum;
+  for (int cb = 0; cb < CB; ++cb) {
+    const int col = cb * 16 + l16;
+    const int mem = col / a.G;
+    valid[cb] = mem < count;
+    req[cb] = valid[cb] ? j.perm[first + mem] : 0;
+    if ((unsigned)req[cb] >= (unsigned)a.B) {
+      if (a.err) rkv::raise_flag(a.err);
+      valid[cb] = false;
+      req[cb] = 0;
     }
+    head[cb] = g * a.G + col % a.G;
+    load_q<D>(a.q, (int64_t)req[cb] * a.hq + head[cb], valid[cb], qreg[cb]);
+  }
+  State<D, CB> st;
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) st.o[cb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st.l[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st.m[cb] = -INFINITY;
+  }
+  walk<D, CB>(a, a.r2t + (int64_t)rep * a.ld, kb, ke, g, qreg, ncb, st, Vs);
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    if (!valid[cb]) continue;
+    const int r = req[cb];
+    const int r0 = a.rec_indptr[r], r1 = a.rec_indptr[r + 1];
+    const int rec = r0 + rec_off;
+    if (r0 < 0 || rec >= r1 || r1 > a.n_records || !a.ws) {
+      if (a.err) rkv::raise_flag(a.err);
+      continue;
+    }
+    store_partial<D>(ws_row(a, D, r, head[cb], rec), st.o[cb], st.m[cb], st.l[cb][0]);
   }
 }
 
@@ -503,14 +670,26 @@ __global__ __launch_bounds__(64) void decode_merge(DecodeArgs a) {
   const int64_t w = blockIdx.x;
   const int r = (int)(w / a.hq);
   const int head = (int)(w % a.hq);
-  const int L = min(a.seq_lens[r], a.max_seq_len);
-  const int chunk = split_chunk(L, a.num_splits);
-  const int nsplit = (L + chunk - 1) / chunk;
+  // partials: plain layout = this request's splits; prefix-shared layout =
+  // its records (shared ranges first, then the tail splits)
+  int nsplit, rec0;
+  if (a.rec_indptr) {
+    rec0 = a.rec_indptr[r];
+    const int r1 = a.rec_indptr[r + 1];
+    if (rec0 < 0 || r1 > a.n_records || !a.ws) return;     // reported by phase 1
+    nsplit = r1 - rec0;
+  } else {
+    const int L = min(a.seq_lens[r], a.max_seq_len);
+    const int chunk = split_chunk(L, a.num_splits);
+    nsplit = (L + chunk - 1) / chunk;
+    rec0 = 0;
+  }
   if (nsplit <= 1) return;
   const int lane = threadIdx.x;
-  const float* src = a.ws + ((int64_t)r * a.hq + head) * a.splits * (D + 4);
+  const float* src = ws_row(a, D, r, head, rec0);
+  const int64_t stride = a.rec_indptr ? (int64_t)a.hq * (D + 4) : (D + 4);
   float M = -INFINITY;
-  for (int s = lane; s < nsplit; s += 64) M = fmaxf(M, src[(int64_t)s * (D + 4) + D]);
+  for (int s = lane; s < nsplit; s += 64) M = fmaxf(M, src[(int64_t)s * stride + D]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   constexpr int PER = D / 64;
@@ -519,7 +698,7 @@ __global__ __launch_bounds__(64) void decode_merge(DecodeArgs a) {
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
   float lsum = 0.f;
   for (int s = 0; s < nsplit; ++s) {
-    const float* p = src + (int64_t)s * (D + 4);
+    const float* p = src + (int64_t)s * stride;
     const float ms = p[D];
     const float f = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
     lsum += p[D + 1] * f;
@@ -560,6 +739,43 @@ void launch_all(const DecodeArgs& a, int64_t grid, hipStream_t st) {
   else if (g <= 4) launch_partial<T, D, 4>(a, grid, st);
   else launch_partial<T, D, 8>(a, grid, st);
   hipLaunchKernelGGL((decode_merge<T, D>), dim3((unsigned)((int64_t)a.B * a.hq)), dim3(64), 0, st, a);
+}
+
+// Query columns per prefix-shared wave: two 16-column blocks at D = 128 and
+// four at D = 64 fit two waves per SIMD without spills.
+constexpr int kMaxSharedColumns(int d) { return d == 128 ? 32 : 64; }
+
+template <int D, int CB>
+void launch_shared(const DecodeArgs& a, const SharedJobs& j, hipStream_t st) {
+  int64_t grid = (int64_t)j.n_jobs * a.hkv;
+  grid = (grid + rkv::kXcds - 1) / rkv::kXcds * rkv::kXcds;
+  hipLaunchKernelGGL((decode_shared<D, CB>), dim3((unsigned)grid), dim3(64), 0, st, a, j);
+}
+
+template <int D>
+void launch_cascade(const DecodeArgs& a, const SharedJobs& j, int cb, hipStream_t st) {
+  if (j.n_jobs > 0) {
+    if (cb <= 1) launch_shared<D, 1>(a, j, st);
+    else if (cb <= 2 || D == 128) launch_shared<D, 2>(a, j, st);
+    else if constexpr (D == 64) launch_shared<D, 4>(a, j, st);
+  }
+  int64_t grid = (int64_t)a.splits * a.B * ((a.hkv + a.hb - 1) / a.hb) * a.hg;
+  grid = (grid + rkv::kXcds - 1) / rkv::kXcds * rkv::kXcds;
+  launch_all<uint16_t, D>(a, grid, st);
+}
+
+// kv heads per workgroup of the vector kernel (a power of two, at most 4):
+// a key's rows for them are one contiguous run of the slot, and
+// 256 / (hb * lpr) keys are read per instruction.  Measured on the 32-head
+// decode batches: 4 heads (1 KB runs, 4 keys per instruction) beat 16 (4 KB
+// runs, 1 key) by 5-8 %, and 2 or 1 heads; more distinct slots in flight
+// spread better over HBM.
+int heads_per_block(int d, int dtype, int hkv) {
+  const int lpr = d * (dtype == RKV_BF16 ? 2 : 4) / 16;
+  int hb = 256 / lpr;
+  if (hb > 4) hb = 4;
+  while (hb > 1 && hb / 2 >= hkv) hb /= 2;
+  return hb;
 }
 
 int64_t splits_extent(int32_t max_seq_len, int32_t num_splits) {
@@ -603,23 +819,16 @@ extern "C" int rkv_attn_decode(const void* q, const void* k_pool, const void* v_
   a.B = B; a.hq = hq; a.hkv = hkv; a.G = hq / hkv;
   a.hg = (a.G + kMaxG - 1) / kMaxG;
   a.max_seq_len = max_seq_len;
-  {
-    // kv heads per workgroup (a power of two, at most 4): a key's rows for
-    // them are one contiguous run of the slot, and 256 / (hb * lpr) keys are
-    // read per instruction.  Measured on the 32-head decode batches: 4 heads
-    // (1 KB runs, 4 keys per instruction) beat 16 (4 KB runs, 1 key) by 5-8 %,
-    // and 2 or 1 heads; more distinct slots in flight spread better over HBM.
-    const int lpr = d * (dtype == RKV_BF16 ? 2 : 4) / 16;
-    int hb = 256 / lpr;
-    if (hb > 4) hb = 4;
-    while (hb > 1 && hb / 2 >= hkv) hb /= 2;
-    a.hb = hb;
-  }
+  a.hb = heads_per_block(d, dtype, hkv);
   a.splits = (int32_t)S;
   a.num_splits = num_splits;
   a.scale_log2e = sm_scale * 1.4426950408889634f;
   a.pool_slots = pool_slots;
   a.ws = (float*)workspace;
+  a.rec_indptr = nullptr;
+  a.tail_begin = nullptr;
+  a.n_records = 0;
+  a.tail_chunk = 0;
   if (int rc = rkv::debug_flag(&a.err)) return rc;
   int64_t grid = (int64_t)S * B * ((hkv + a.hb - 1) / a.hb) * a.hg;
   grid = (grid + rkv::kXcds - 1) / rkv::kXcds * rkv::kXcds;
@@ -631,4 +840,71 @@ extern "C" int rkv_attn_decode(const void* q, const void* k_pool, const void* v_
     if (d == 128) launch_all<float, 128>(a, grid, st); else launch_all<float, 64>(a, grid, st);
   }
   return rkv::finish_launch("rkv_attn_decode", st, a.err);
+}
+
+extern "C" size_t rkv_attn_decode_cascade_workspace_bytes(int64_t n_records, int32_t hq, int32_t d) {
+  if (n_records < 0 || hq < 1 || (d != 64 && d != 128)) return 0;
+  return (size_t)n_records * hq * (d + 4) * sizeof(float);
+}
+
+extern "C" int rkv_attn_decode_cascade(const void* q, const void* k_pool, const void* v_pool, void* o,
+                                       float* lse, const int32_t* req_to_token, int64_t ld,
+                                       const int32_t* seq_lens, int32_t B, int32_t max_seq_len, int32_t hq,
+                                       int32_t hkv, int32_t d, float sm_scale, int32_t dtype,
+                                       const int32_t* perm, const int32_t* rec_indptr,
+                                       const int32_t* tail_begin, const int32_t* jobs, int64_t n_jobs,
+                                       int32_t max_members, int32_t tail_chunk, int32_t tail_splits,
+                                       int64_t n_records, void* workspace, size_t ws_bytes,
+                                       int64_t pool_slots, void* stream) {
+  rkv::clear_error();
+  if (B < 0 || hq < 1 || hkv < 1 || max_seq_len < 1 || ld < max_seq_len || pool_slots < 1 ||
+      !(sm_scale > 0.f) || n_jobs < 0 || max_members < 1 || tail_chunk < 1 || tail_splits < 0 ||
+      n_records < 0 || n_records > 0x7fffffff || n_jobs > 0x7fffffff)
+    return rkv::fail(RKV_EINVAL, "rkv_attn_decode_cascade: bad sizes");
+  if (dtype != RKV_BF16) return rkv::fail(RKV_ENOTSUP, "rkv_attn_decode_cascade: bf16 only");
+  if (d != 64 && d != 128) return rkv::fail(RKV_ENOTSUP, "rkv_attn_decode_cascade: head_dim must be 64 or 128");
+  if (hq % hkv != 0 || hq / hkv > 16)
+    return rkv::fail(RKV_ENOTSUP, "rkv_attn_decode_cascade: Hq/Hkv must be an integer <= 16");
+  const int G = hq / hkv;
+  if ((int64_t)max_members * G > kMaxSharedColumns(d))
+    return rkv::fail(RKV_ENOTSUP, "rkv_attn_decode_cascade: max_members * Hq/Hkv must be <= " +
+                                      std::to_string(kMaxSharedColumns(d)));
+  if (B == 0) return RKV_OK;
+  if (!q || !k_pool || !v_pool || !o || !req_to_token || !seq_lens || !perm || !rec_indptr || !tail_begin ||
+      (n_jobs > 0 && !jobs))
+    return rkv::fail(RKV_EINVAL, "rkv_attn_decode_cascade: NULL pointer");
+  const uintptr_t al = (uintptr_t)q | (uintptr_t)k_pool | (uintptr_t)v_pool | (uintptr_t)o;
+  if (al & 15) return rkv::fail(RKV_EINVAL, "rkv_attn_decode_cascade: tensors must be 16-byte aligned");
+  const size_t need = rkv_attn_decode_cascade_workspace_bytes(n_records, hq, d);
+  if ((n_records > B || n_jobs > 0) && (!workspace || ws_bytes < need || ((uintptr_t)workspace & 15)))
+    return rkv::fail(RKV_EINVAL, "rkv_attn_decode_cascade: workspace missing or too small");
+  if (tail_splits < 1) return rkv::fail(RKV_EINVAL, "rkv_attn_decode_cascade: tail_splits must be >= 1");
+  DecodeArgs a;
+  a.q = q; a.kp = k_pool; a.vp = v_pool; a.o = o; a.lse = lse;
+  a.r2t = req_to_token; a.ld = ld; a.seq_lens = seq_lens;
+  a.B = B; a.hq = hq; a.hkv = hkv; a.G = G;
+  a.hg = (G + kMaxG - 1) / kMaxG;
+  a.max_seq_len = max_seq_len;
+  a.hb = heads_per_block(d, dtype, hkv);
+  a.splits = tail_splits;
+  a.num_splits = 0;
+  a.scale_log2e = sm_scale * 1.4426950408889634f;
+  a.pool_slots = pool_slots;
+  a.ws = (float*)workspace;
+  a.rec_indptr = rec_indptr;
+  a.tail_begin = tail_begin;
+  a.n_records = (int32_t)n_records;
+  a.tail_chunk = tail_chunk;
+  if (int rc = rkv::debug_flag(&a.err)) return rc;
+  SharedJobs j;
+  j.jobs = jobs;
+  j.perm = perm;
+  j.n_jobs = (int32_t)n_jobs;
+  j.max_members = max_members;
+  const int cb = (max_members * G + 15) / 16;
+  if ((int64_t)n_jobs * hkv > 0x7fffffff || (int64_t)tail_splits * B * hkv > 0x7fffffff)
+    return rkv::fail(RKV_ENOTSUP, "rkv_attn_decode_cascade: grid too large");
+  hipStream_t st = (hipStream_t)stream;
+  if (d == 128) launch_cascade<128>(a, j, cb, st); else launch_cascade<64>(a, j, cb, st);
+  return rkv::finish_launch("rkv_attn_decode_cascade", st, a.err);
 }

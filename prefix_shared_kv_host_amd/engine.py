@@ -82,8 +82,9 @@ class RadixKVCache:
                         batch.prefix_lens, batch.max_new, lse=lse, stream=stream)
         return o
 
-    def workspace(self, B, hq, max_len, num_splits=0):
-        need = rkv.attn_decode_workspace_bytes(B, hq, self.d, max_len, num_splits)
+    def workspace(self, B, hq, max_len, num_splits=0, need=None):
+        if need is None:
+            need = rkv.attn_decode_workspace_bytes(B, hq, self.d, max_len, num_splits)
         if self._ws is None or self._ws.numel() * 4 < need:
             self._ws = torch.empty(max(need // 4, 1), dtype=torch.float32, device=self.device)
         return self._ws
@@ -95,4 +96,26 @@ class RadixKVCache:
         ws = self.workspace(B, hq, batch.max_len, num_splits)
         rkv.attn_decode(q, self.k_pool, self.v_pool, o, batch.req_to_token, batch.seq_lens,
                         batch.max_len, ws, lse=lse, num_splits=num_splits, stream=stream)
+        return o
+
+    def cascade_plan(self, batch: Batch, hq, seg_chunk=256, tail_chunk=768, min_keys=32, max_members=None):
+        """Plans prefix-shared decode from the batch's host tables and copies
+        the plan to the device."""
+        mm = rkv.cascade_max_members(hq, self.hkv, self.d) if max_members is None else max_members
+        plan = rkv.cascade_plan(batch.host["req_to_token"], batch.host["seq_lens"], seg_chunk, tail_chunk,
+                                min_keys, mm)
+        return plan.to(self.device)
+
+    def decode_cascade(self, batch: Batch, q, plan=None, o=None, lse=None, stream=None, **plan_args):
+        """Decode that reads each run of keys shared by several requests of
+        the batch once (plan from cascade_plan, made here when not given)."""
+        if o is None:
+            o = torch.empty_like(q)
+        B, hq, _ = q.shape
+        if plan is None:
+            plan = self.cascade_plan(batch, hq, **plan_args)
+        ws = self.workspace(B, hq, batch.max_len,
+                            need=rkv.attn_decode_cascade_workspace_bytes(plan.n_records, hq, self.d))
+        rkv.attn_decode_cascade(q, self.k_pool, self.v_pool, o, batch.req_to_token, batch.seq_lens,
+                                batch.max_len, plan, ws, lse=lse, stream=stream)
         return o

@@ -29,7 +29,8 @@ EXPORTS = (
     "rkv_radix_lock", "rkv_radix_unlock", "rkv_radix_insert", "rkv_radix_evict", "rkv_alloc",
     "rkv_free", "rkv_stats", "rkv_radix_serialize", "rkv_free_list", "rkv_batch_prepare",
     "rkv_batch_commit", "rkv_kv_scatter", "rkv_attn_extend", "rkv_attn_decode_workspace_bytes",
-    "rkv_attn_decode", "rkv_radix_peek", "rkv_schedule",
+    "rkv_attn_decode", "rkv_radix_peek", "rkv_schedule", "rkv_cascade_plan",
+    "rkv_attn_decode_cascade_workspace_bytes", "rkv_attn_decode_cascade",
 )
 
 
@@ -81,6 +82,12 @@ def lib():
         "rkv_attn_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
         "rkv_attn_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32, _i32, _i32, _i32,
                                            _i32, _f32, _i32, _i32, _vp, _sz, _i64, _vp]),
+        "rkv_cascade_plan": (ctypes.c_int, [c_i32p, _i64, c_i32p, _i32, _i32, _i32, _i32, _i32, c_i32p,
+                                            c_i32p, c_i32p, c_i32p, _i64, c_i64p, c_i32p]),
+        "rkv_attn_decode_cascade_workspace_bytes": (_sz, [_i64, _i32, _i32]),
+        "rkv_attn_decode_cascade": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32, _i32, _i32,
+                                                   _i32, _i32, _f32, _i32, _vp, _vp, _vp, _vp, _i64, _i32,
+                                                   _i32, _i32, _i64, _vp, _sz, _i64, _vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -333,3 +340,76 @@ def attn_decode(q, k_pool, v_pool, o, req_to_token, seq_lens, max_seq_len, works
         int(req_to_token.shape[1]), _ptr(seq_lens), int(B), int(max_seq_len), int(hq), int(hkv),
         int(d), scale, _dtype_code(q), int(num_splits), _ptr(workspace), int(ws_bytes), int(P),
         _stream(stream)))
+
+
+class CascadePlan:
+    """Host arrays of a prefix-shared decode plan (rkv_cascade_plan):
+    perm [B], rec_indptr [B+1], tail_begin [B], jobs [n_jobs, 5] (int32
+    NumPy), with tail_splits, n_records, max_members and tail_chunk."""
+
+    def __init__(self, perm, rec_indptr, tail_begin, jobs, tail_splits, max_members, tail_chunk):
+        self.perm, self.rec_indptr, self.tail_begin, self.jobs = perm, rec_indptr, tail_begin, jobs
+        self.tail_splits, self.max_members, self.tail_chunk = int(tail_splits), int(max_members), int(tail_chunk)
+        self.n_records = int(rec_indptr[-1])
+        self.n_jobs = int(jobs.shape[0])
+        self.dev = None
+
+    def to(self, device):
+        """Copies the arrays to `device` (int32 torch tensors); returns self."""
+        import torch
+        self.dev = {k: torch.from_numpy(np.ascontiguousarray(v)).to(device)
+                    for k, v in (("perm", self.perm), ("rec_indptr", self.rec_indptr),
+                                 ("tail_begin", self.tail_begin), ("jobs", self.jobs.reshape(-1)))}
+        return self
+
+
+def cascade_max_members(hq, hkv, d) -> int:
+    """Largest max_members rkv_attn_decode_cascade accepts for these heads."""
+    return max(1, (32 if int(d) == 128 else 64) // (int(hq) // int(hkv)))
+
+
+def cascade_plan(req_to_token, seq_lens, seg_chunk=256, tail_chunk=768, min_keys=32, max_members=32):
+    """Plans prefix-shared decode from the host table (NumPy int32 [B, ld]
+    and seq_lens [B]).  Returns a CascadePlan."""
+    r2t = np.ascontiguousarray(np.asarray(req_to_token, dtype=np.int32))
+    L = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    B = int(L.shape[0])
+    ld = int(r2t.shape[1]) if r2t.ndim == 2 else 0
+    perm = np.empty(max(B, 1), dtype=np.int32)
+    rec = np.empty(B + 1, dtype=np.int32)
+    tb = np.empty(max(B, 1), dtype=np.int32)
+    n_jobs, tail = _i64(), _i32()
+    args = lambda jobs, cap: (r2t.ctypes.data_as(c_i32p), ld, L.ctypes.data_as(c_i32p), B, int(seg_chunk),
+                              int(tail_chunk), int(min_keys), int(max_members), perm.ctypes.data_as(c_i32p),
+                              rec.ctypes.data_as(c_i32p), tb.ctypes.data_as(c_i32p), jobs, cap,
+                              ctypes.byref(n_jobs), ctypes.byref(tail))
+    code = lib().rkv_cascade_plan(*args(None, 0))
+    if code not in (OK, ENOSPC):
+        _check(code)
+    jobs = np.empty((max(n_jobs.value, 1), 5), dtype=np.int32)
+    _check(lib().rkv_cascade_plan(*args(jobs.ctypes.data_as(c_i32p), n_jobs.value)))
+    return CascadePlan(perm[:B], rec, tb[:B], jobs[: n_jobs.value], tail.value, max_members, tail_chunk)
+
+
+def attn_decode_cascade_workspace_bytes(n_records, hq, d) -> int:
+    return int(lib().rkv_attn_decode_cascade_workspace_bytes(int(n_records), int(hq), int(d)))
+
+
+def attn_decode_cascade(q, k_pool, v_pool, o, req_to_token, seq_lens, max_seq_len, plan, workspace, lse=None,
+                        sm_scale=None, stream=None):
+    """Prefix-shared decode of q [B, Hq, D] following `plan` (a CascadePlan
+    already copied to the device with plan.to(device))."""
+    _need_cuda(q, k_pool, v_pool, o, req_to_token, seq_lens, lse, workspace)
+    if plan.dev is None:
+        raise RkvError(EINVAL, "the plan's arrays are not on the device (call plan.to(device))")
+    B, hq, d = q.shape
+    P, hkv, _ = k_pool.shape
+    scale = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    dv = plan.dev
+    return _check(lib().rkv_attn_decode_cascade(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(o), _ptr(lse), _ptr(req_to_token),
+        int(req_to_token.shape[1]), _ptr(seq_lens), int(B), int(max_seq_len), int(hq), int(hkv), int(d),
+        scale, _dtype_code(q), _ptr(dv["perm"]), _ptr(dv["rec_indptr"]), _ptr(dv["tail_begin"]),
+        _ptr(dv["jobs"]) if plan.n_jobs else None, plan.n_jobs, plan.max_members, plan.tail_chunk,
+        plan.tail_splits, plan.n_records, _ptr(workspace), int(ws_bytes), int(P), _stream(stream)))

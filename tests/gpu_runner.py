@@ -60,9 +60,11 @@ def needed_slots(shape, phases, select):
 
 
 def run(shape, phases, select=lambda i, B: None, num_splits=0, content_device="cuda",
-        with_lse=True, sparse=False):
+        with_lse=True, sparse=False, cascade=None):
     """Returns a list of per-checked-phase dicts with GPU and oracle outputs
-    restricted to the selected requests' rows."""
+    restricted to the selected requests' rows.  cascade: None for plain
+    decode, else a dict of cascade_plan arguments for prefix-shared decode
+    (the native plan is then asserted equal to the oracle's)."""
     from prefix_shared_kv_host_amd.engine import RadixKVCache
 
     dt = content.torch_dtype(shape.dtype)
@@ -103,6 +105,10 @@ def run(shape, phases, select=lambda i, B: None, num_splits=0, content_device="c
             lse = torch.full((rows, shape.hq), float("nan"), device="cuda") if with_lse else None
             if ph.kind == "extend":
                 o = cache.extend(batch, qd, lse=lse)
+            elif cascade is not None:
+                plan = cache.cascade_plan(batch, shape.hq, **cascade)
+                check_plan(plan, otb, **cascade)
+                o = cache.decode_cascade(batch, qd, plan=plan, lse=lse)
             else:
                 o = cache.decode(batch, qd, lse=lse, num_splits=num_splits)
             torch.cuda.synchronize()
@@ -126,6 +132,20 @@ def run(shape, phases, select=lambda i, B: None, num_splits=0, content_device="c
         otree.batch_commit(ph.seqs, otb["req_to_token"], otb["nodes"])
         cache.commit(batch)
     return out, cache
+
+
+def check_plan(plan, otb, seg_chunk=256, tail_chunk=768, min_keys=32, max_members=None):
+    """The native prefix-shared plan equals the oracle's, array by array."""
+    from oracle import cascade as ocas
+    L = otb["seq_lens"]
+    ref = ocas.plan([row[: int(L[r])] for r, row in enumerate(otb["req_to_token"])], L, seg_chunk,
+                    tail_chunk, min_keys, plan.max_members)
+    assert plan.perm.tolist() == ref["perm"]
+    assert plan.rec_indptr.tolist() == ref["rec_indptr"]
+    assert plan.tail_begin.tolist() == ref["tail_begin"]
+    assert [tuple(j) for j in plan.jobs.tolist()] == ref["jobs"]
+    assert plan.tail_splits == ref["tail_splits"]
+    log(f"  plan: {plan.n_jobs} jobs, {plan.n_records} records, tail splits {plan.tail_splits}")
 
 
 def check(res, dtype, name=""):

@@ -1,0 +1,94 @@
+"""GPU parity of prefix-shared ("cascade") decode (rkv_attn_decode_cascade)
+against the float64 oracle's plain decode attention, with the native plan
+asserted equal to the oracle's plan on every batch.
+
+Workloads: random prefix trees of decode requests (several sharing levels,
+identical histories, one-token requests, ragged lengths) over every
+query-per-kv-head ratio the MFMA phase handles and both head dims, with plan
+settings that exercise folding, short chunks, ragged tails and member groups
+of one; then sampled requests of the radix-tree decode batch (256 requests),
+its no-share control (no shared run: tails only) and the grouped-head decode
+batch (64 requests under one 2048-token prefix).  Tolerances as for plain
+decode: max-abs 2e-2 on o, lse within ln(1 + 2^-8) (weights rounded to bf16
+on the matrix cores)."""
+import numpy as np
+import pytest
+import torch
+
+from inputs import configs
+from tests import gpu_runner as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from prefix_shared_kv_host_amd import rkv
+    rkv.lib()
+    G.log(f"device: {torch.cuda.get_device_name(0)}")
+
+
+def tree_decode_workload(seed, B=24, max_len=1400):
+    """Histories cached in a setup batch, then one decode batch.  Request i
+    copies a cut of an earlier request's history (often at a deep point, so
+    runs nest several levels) and appends fresh tokens; a few copy a whole
+    history (identical rows but the query key); some are one token long."""
+    rng = np.random.default_rng(seed)
+    hist = []
+    for i in range(B):
+        if i >= 2 and i % 11 == 0:
+            h = list(hist[int(rng.integers(len(hist)))])
+        elif i % 13 == 5:
+            h = []
+        elif hist and rng.random() < 0.8:
+            base = hist[int(rng.integers(len(hist)))]
+            cut = int(rng.integers(len(base) // 3, len(base) + 1)) if base else 0
+            n = int(rng.integers(1, 400))
+            h = base[:cut] + [int(x) for x in rng.integers(0, 32000, n)]
+            if cut < len(base):
+                h[cut] = 60000 + i                     # branch off at the cut
+        else:
+            h = [int(x) for x in rng.integers(0, 32000, int(rng.integers(2, max_len)))]
+            h[0] = 70000 + i
+        hist.append(h[:max_len])
+    full = [h + [80000 + i] for i, h in enumerate(hist)]
+    return [configs.Phase("setup", [h for h in hist if h]), configs.Phase("decode", full)]
+
+
+CASES = [
+    # hq, hkv, d, plan settings
+    (4, 4, 128, dict(seg_chunk=256, tail_chunk=768, min_keys=32)),
+    (4, 4, 128, dict(seg_chunk=100, tail_chunk=128, min_keys=1)),
+    (8, 4, 64, dict(seg_chunk=64, tail_chunk=200, min_keys=8)),
+    (8, 2, 128, dict(seg_chunk=256, tail_chunk=768, min_keys=32)),
+    (16, 2, 128, dict(seg_chunk=96, tail_chunk=320, min_keys=1, max_members=1)),
+    (16, 1, 64, dict(seg_chunk=256, tail_chunk=512, min_keys=16)),
+    (12, 2, 128, dict(seg_chunk=160, tail_chunk=768, min_keys=4)),
+    (3, 1, 128, dict(seg_chunk=256, tail_chunk=384, min_keys=32, max_members=3)),
+    (2, 2, 64, dict(seg_chunk=32, tail_chunk=64, min_keys=1)),
+]
+
+
+@pytest.mark.parametrize("hq,hkv,d,plan", CASES)
+def test_cascade_tree_decode(hq, hkv, d, plan):
+    shape = configs.Shape(f"cas-{hq}-{hkv}-{d}", hq, hkv, d, "bf16", 1 << 16, 51)
+    phases = tree_decode_workload(seed=hq * 100 + d + plan["tail_chunk"])
+    res, _ = G.run(shape, phases, content_device="cpu", cascade=plan)
+    G.check(res, "bf16", f"cascade {hq}/{hkv} d{d} {plan}")
+
+
+@pytest.mark.timeout(400)
+@pytest.mark.parametrize("name", ["c3", "c3ns"])
+def test_cascade_c3_sampled(name):
+    shape, phases = configs.build(name)
+    res, _ = G.run(shape, phases, select=G.sample(5, 24), sparse=True, cascade={})
+    G.check(res, "bf16", f"{name} cascade")
+
+
+@pytest.mark.timeout(400)
+def test_cascade_c4_decode_sampled():
+    shape, phases = configs.c4()
+    ph = [phases[0], phases[1], phases[3]]
+    res, _ = G.run(shape, ph, select=G.sample(6, 16), sparse=True, cascade={})
+    G.check(res, "bf16", "c4-decode cascade")
