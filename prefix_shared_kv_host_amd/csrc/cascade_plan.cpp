@@ -24,6 +24,7 @@
 
 #include <algorithm>
 #include <climits>
+#include <cstring>
 #include <string>
 #include <vector>
 
@@ -31,6 +32,15 @@
 #include "rkv_internal.h"
 
 namespace {
+
+// First position where a[0..n) and b[0..n) differ (n if none): 64-byte
+// blocks by memcmp, then element by element inside the first differing block.
+inline int32_t mismatch_at(const int32_t* a, const int32_t* b, int32_t n) {
+  int32_t i = 0;
+  while (i + 16 <= n && std::memcmp(a + i, b + i, 64) == 0) i += 16;
+  while (i < n && a[i] == b[i]) ++i;
+  return i;
+}
 
 struct Frame {
   int32_t lo, hi;        // block of sorted positions
@@ -60,14 +70,17 @@ extern "C" int rkv_cascade_plan(const int32_t* req_to_token, int64_t ld, const i
 
   std::vector<int32_t> order(B);
   for (int32_t r = 0; r < B; ++r) order[r] = r;
+  // lexicographic order of the truncated rows as int32 sequences
   std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
-    return std::lexicographical_compare(row(a), row(a) + len(a), row(b), row(b) + len(b));
+    const int32_t n = std::min(len(a), len(b));
+    const int32_t i = mismatch_at(row(a), row(b), n);
+    return i < n ? row(a)[i] < row(b)[i] : len(a) < len(b);
   });
   std::vector<int32_t> lcp(B > 0 ? B : 1, 0);
   for (int32_t i = 1; i < B; ++i) {
     const int32_t a = order[i - 1], b = order[i];
     const int32_t n = std::min(len(a), len(b));
-    lcp[i] = (int32_t)(std::mismatch(row(a), row(a) + n, row(b)).first - row(a));
+    lcp[i] = mismatch_at(row(a), row(b), n);
   }
 
   std::vector<int32_t> job;                 // 5 values per job

@@ -28,6 +28,7 @@
 #include <stdint.h>
 
 #include <string>
+#include <type_traits>
 
 #include "device.h"
 #include "rkv.h"
@@ -162,188 +163,6 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float* acc, floa
   m = M;
 }
 
-// Phase 1.  Work item = (request, split, block of HB kv heads [, q-head
-// group]).  A key's rows for the HB heads are HB*D contiguous elements of the
-// slot, so the workgroup reads them as one contiguous run: lane group
-// (LPR lanes) hl handles kv head hb*HB + hl, and RPI = 256/(HB*LPR) keys are
-// read per instruction (one per row group ri, which is wave-uniform, so the
-// slot index is a scalar load).  Each lane group walks the keys of the split
-// with its own fp32 online softmax; row groups (RPI > 1) merge in LDS.
-template <typename T, int D, int G, int U>
-__global__ __launch_bounds__(256) void decode_partial(DecodeArgs a) {
-  using E = Elem<T>;
-  constexpr int VEC = E::kVec;
-  constexpr int LPR = D / VEC;          // lanes per (slot, kv head) row
-  static_assert(LPR >= 8 && LPR <= 32, "row width");
-  const int HB = a.hb;                  // kv heads per workgroup
-  const int RPI = 256 / (HB * LPR);     // keys per instruction (row groups)
-
-  const int64_t w = rkv::xcd_work_item(blockIdx.x, gridDim.x);
-  // item order: (head block, sub-group) outermost, then request, then split,
-  // so neighbouring requests (siblings in the tree) share an XCD
-  const int s = (int)(w % a.splits);
-  int64_t rest = w / a.splits;
-  const int r = (int)(rest % a.B);
-  rest /= a.B;
-  const int sub = (int)(rest % a.hg);
-  const int hblk = (int)(rest / a.hg);
-  if (hblk * HB >= a.hkv) return;
-  const int L = min(a.seq_lens[r], a.max_seq_len);
-  int k_begin, k_end, rec, nsplit;
-  if (!split_span(a, r, s, L, k_begin, k_end, rec, nsplit)) return;
-  const int h0 = sub * kMaxG;                   // first q head of this group within a kv group
-  const int nh = min(G, a.G - h0);              // q heads handled here (<= G)
-
-  const int tid = threadIdx.x;
-  const int lr = tid % LPR;                     // lane within row
-  const int hl = (tid / LPR) % HB;              // kv head within the block
-  // row group; wave-uniform (scalar slot loads) when a row group spans whole waves
-  const int ri = (HB * LPR >= 64) ? __builtin_amdgcn_readfirstlane(tid / (HB * LPR)) : tid / (HB * LPR);
-  const int g = hblk * HB + hl;                 // kv head of this lane group
-  const bool gvalid = g < a.hkv;
-  const int gg = gvalid ? g : a.hkv - 1;
-
-  // queries, pre-scaled into the log2 domain
-  float qv[G][VEC];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    const int qh = min(hh, nh - 1);
-    const int64_t qoff = ((int64_t)r * a.hq + (int64_t)gg * a.G + h0 + qh) * D + lr * VEC;
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) qv[hh][e] = E::load1(a.q, qoff + e) * a.scale_log2e;
-  }
-  float m[G], l[G], acc[G][VEC];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    m[hh] = -INFINITY;
-    l[hh] = 0.f;
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[hh][e] = 0.f;
-  }
-
-  const int32_t* row_tab = a.r2t + (int64_t)r * a.ld;
-  const uint32_t P = (uint32_t)min(a.pool_slots, (int64_t)0x7fffffff);
-  const uint32_t slot_bytes = (uint32_t)a.hkv * D * (uint32_t)sizeof(T);
-  const char* kbase = (const char*)a.kp + ((uint64_t)gg * LPR + lr) * 16;
-  const char* vbase = (const char*)a.vp + ((uint64_t)gg * LPR + lr) * 16;
-  const int step = U * RPI;
-
-  // slot indices run one iteration ahead of the K/V gathers that use them
-  int32_t slots[U];
-  auto fetch_slots = [&](int base) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) slots[u] = row_tab[min(base + u * RPI + ri, k_end - 1)];
-  };
-  fetch_slots(k_begin);
-  for (int base = k_begin; base < k_end; base += step) {
-    uint4 kr[U], vr[U];
-    bool ok[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int key = base + u * RPI + ri;       // wave-uniform
-      ok[u] = key < k_end;
-      int32_t slot = slots[u];
-      if ((uint32_t)slot >= P) {
-        if (a.err) rkv::raise_flag(a.err);
-        ok[u] = false;
-        slot = 0;
-      }
-      const uint64_t off = (uint64_t)(uint32_t)slot * slot_bytes;
-      kr[u] = *(const uint4*)(kbase + off);
-      vr[u] = *(const uint4*)(vbase + off);
-    }
-    if (base + step < k_end) fetch_slots(base + step);
-    float sc[U][G];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float kf[VEC];
-      E::unpack(kr[u], kf);
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        float t = 0.f;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) t = fmaf(qv[hh][e], kf[e], t);
-        sc[u][hh] = rkv::group_sum<LPR>(t);
-      }
-    }
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (!ok[u]) sc[u][hh] = -INFINITY;
-        mx = fmaxf(mx, sc[u][hh]);
-      }
-      const float mn = fmaxf(m[hh], mx);
-      const float mref = (mn == -INFINITY) ? 0.f : mn;
-      const float alpha = __builtin_amdgcn_exp2f(m[hh] - mref);
-      l[hh] *= alpha;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[hh][e] *= alpha;
-      m[hh] = mn;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float p = __builtin_amdgcn_exp2f(sc[u][hh] - mref);
-        l[hh] += p;
-        float vf[VEC];
-        E::unpack(vr[u], vf);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[hh][e] = fmaf(p, vf[e], acc[hh][e]);
-      }
-    }
-  }
-
-  // row groups (RPI > 1) merge in LDS: [row group][head in block][G][D + 2]
-  extern __shared__ float red[];
-  if (RPI > 1) {
-    if (ri > 0) {
-      float* dst = red + (((ri - 1) * HB + hl) * G) * (D + 2);
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) dst[hh * (D + 2) + lr * VEC + e] = acc[hh][e];
-        if (lr == 0) {
-          dst[hh * (D + 2) + D] = m[hh];
-          dst[hh * (D + 2) + D + 1] = l[hh];
-        }
-      }
-    }
-    __syncthreads();
-    if (ri > 0) return;
-    for (int rr = 1; rr < RPI; ++rr) {
-      const float* src = red + (((rr - 1) * HB + hl) * G) * (D + 2);
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        float ab[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) ab[e] = src[hh * (D + 2) + lr * VEC + e];
-        merge_state(m[hh], l[hh], acc[hh], src[hh * (D + 2) + D], src[hh * (D + 2) + D + 1], ab, VEC);
-      }
-    }
-  }
-  if (!gvalid) return;
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    if (hh >= nh) break;
-    const int head = g * a.G + h0 + hh;
-    if (rec < 0) {
-      const float inv = 1.f / l[hh];
-      const int64_t ooff = ((int64_t)r * a.hq + head) * D + lr * VEC;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) E::store1(a.o, ooff + e, acc[hh][e] * inv);
-      if (a.lse && lr == 0) a.lse[(int64_t)r * a.hq + head] = (m[hh] + log2f(l[hh])) * 0.69314718055994531f;
-    } else {
-      float* dst = ws_row(a, D, r, head, rec);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) dst[lr * VEC + e] = acc[hh][e];
-      if (lr == 0) {
-        dst[D] = m[hh];
-        dst[D + 1] = l[hh];
-      }
-    }
-  }
-}
-
 // Phase 1 on the matrix cores (bf16): query columns that read the same K/V
 // rows go through v_mfma_f32_16x16x32_bf16 together as the N dimension
 // (S^T = K Q^T, 16 keys x 16 query columns per block).  Two users:
@@ -400,7 +219,7 @@ __device__ __forceinline__ void walk(const DecodeArgs& a, const int32_t* row_tab
   constexpr int STEP = 32;
   constexpr int RPI = 1024 / ROWB;          // V rows per DMA instruction
   constexpr int NDMA = STEP / RPI;          // DMA instructions per step
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int l16 = lane & 15, gq = lane >> 4;
   const float c = a.scale_log2e;
   const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
@@ -528,7 +347,7 @@ __device__ __forceinline__ void walk(const DecodeArgs& a, const int32_t* row_tab
 // Loads the Q^T operand of one column (zeros when the column is unused).
 template <int D>
 __device__ __forceinline__ void load_q(const void* qbase, int64_t row, bool valid, bf16x8 (&out)[D / 32]) {
-  const uint16_t* qp = (const uint16_t*)qbase + row * D + (threadIdx.x >> 4) * 8;
+  const uint16_t* qp = (const uint16_t*)qbase + row * D + ((threadIdx.x & 63) >> 4) * 8;
 #pragma unroll
   for (int k = 0; k < D / 32; ++k) {
     uint4 v = make_uint4(0, 0, 0, 0);
@@ -540,7 +359,7 @@ __device__ __forceinline__ void load_q(const void* qbase, int64_t row, bool vali
 // Writes one column's unnormalised partial (o, max, sum) to a workspace row.
 template <int D>
 __device__ __forceinline__ void store_partial(float* dst, const f32x4 (&o)[D / 16], float m, float l) {
-  const int gq = threadIdx.x >> 4;
+  const int gq = (threadIdx.x & 63) >> 4;
 #pragma unroll
   for (int db = 0; db < D / 16; ++db) *(f32x4*)(dst + db * 16 + 4 * gq) = o[db];
   if (gq == 0) {
@@ -551,11 +370,8 @@ __device__ __forceinline__ void store_partial(float* dst, const f32x4 (&o)[D / 1
 }  // namespace gqa
 
 template <int D>
-__global__ __launch_bounds__(64) void decode_gqa(DecodeArgs a) {
+__device__ __forceinline__ void gqa_item(const DecodeArgs& a, int64_t w, char (&Vs)[2][32 * D * 2]) {
   using namespace gqa;
-  __shared__ __attribute__((aligned(16))) char Vs[2][32 * D * 2];
-
-  const int64_t w = rkv::xcd_work_item(blockIdx.x, gridDim.x);
   const int s = (int)(w % a.splits);
   int64_t rest = w / a.splits;
   const int r = (int)(rest % a.B);
@@ -565,7 +381,7 @@ __global__ __launch_bounds__(64) void decode_gqa(DecodeArgs a) {
   int k_begin, k_end, rec, nsplit;
   if (!split_span(a, r, s, L, k_begin, k_end, rec, nsplit)) return;
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int l16 = lane & 15, gq = lane >> 4;
   const bool hvalid = l16 < a.G;
   const int head = g * a.G + (hvalid ? l16 : 0);
@@ -597,14 +413,10 @@ __global__ __launch_bounds__(64) void decode_gqa(DecodeArgs a) {
 // by side on one XCD.  Column c = cb*16 + l16 is member c / G of the job and
 // q head g*G + c % G.  The plan's values are checked against the batch
 // before use; a job that does not fit is skipped (flag raised in debug mode).
-// Two waves per SIMD: the register budget of 256 per lane holds CB = 2 at
-// D = 128 (without the hint the compiler takes more and runs one wave).
 template <int D, int CB>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_shared(DecodeArgs a, SharedJobs j) {
+__device__ __forceinline__ void shared_item(const DecodeArgs& a, const SharedJobs& j, int64_t w,
+                                            char (&Vs)[2][32 * D * 2]) {
   using namespace gqa;
-  __shared__ __attribute__((aligned(16))) char Vs[2][32 * D * 2];
-
-  const int64_t w = rkv::xcd_work_item(blockIdx.x, gridDim.x);
   const int job = (int)(w % j.n_jobs);
   const int g = (int)(w / j.n_jobs);
   if (g >= a.hkv) return;
@@ -620,8 +432,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     if (g == 0 && a.err) rkv::raise_flag(a.err);
     return;
   }
-  const int lane = threadIdx.x;
-  const int l16 = lane & 15;
+  const int l16 = threadIdx.x & 15;
   const int ncb = (count * a.G + 15) / 16;
   bf16x8 qreg[CB][D / 32];
   int req[CB], head[CB];
@@ -661,6 +472,238 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     }
     store_partial<D>(ws_row(a, D, r, head[cb], rec), st.o[cb], st.m[cb], st.l[cb][0]);
   }
+}
+
+// Phase 1.  Work item = (request, split, block of HB kv heads [, q-head
+// group]).  A key's rows for the HB heads are HB*D contiguous elements of the
+// slot, so the workgroup reads them as one contiguous run: lane group
+// (LPR lanes) hl handles kv head hb*HB + hl, and RPI = 256/(HB*LPR) keys are
+// read per instruction (one per row group ri, which is wave-uniform, so the
+// slot index is a scalar load).  Each lane group walks the keys of the split
+// with its own fp32 online softmax; row groups (RPI > 1) merge in LDS.
+//
+// CB > 0 makes the prefix-shared variant (bf16): blocks [0, shared_blocks)
+// run four shared items each on the matrix cores (one per wave, with its own
+// V stages; see shared_item), the rest run the tail splits as above, so the
+// shared work overlaps the long private tails in one launch.  Each range has
+// its own XCD-aware order.  The body stays in the kernel itself: moved into
+// a device function, the compiler takes 256 + 90 registers for U = 16 and
+// the kernel drops to one wave per SIMD.  The prefix-shared variant asks for
+// two waves per SIMD and runs its tails with U = 8 (242 registers with two
+// shared column blocks); U = 16 under that request spills.
+template <typename T, int D, int G, int U, int CB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CB > 0 ? 2 : 1))) void decode_partial(
+    DecodeArgs a, SharedJobs j, int32_t shared_blocks) {
+  using E = Elem<T>;
+  extern __shared__ float red[];
+  int64_t w;
+  if constexpr (CB > 0) {
+    __shared__ __attribute__((aligned(16))) char Vs[4][2][32 * D * 2];
+    const int b = (int)blockIdx.x;
+    if (b < shared_blocks) {
+      const int wave = (int)(threadIdx.x >> 6);
+      const int64_t item = rkv::xcd_work_item(b, shared_blocks) * 4 + wave;
+      if (item < (int64_t)j.n_jobs * a.hkv) shared_item<D, CB>(a, j, item, Vs[wave]);
+      return;
+    }
+    w = rkv::xcd_work_item(b - shared_blocks, (int64_t)gridDim.x - shared_blocks);
+  } else {
+    w = rkv::xcd_work_item(blockIdx.x, gridDim.x);
+  }
+  constexpr int VEC = E::kVec;
+  constexpr int LPR = D / VEC;          // lanes per (slot, kv head) row
+  static_assert(LPR >= 8 && LPR <= 32, "row width");
+  const int HB = a.hb;                  // kv heads per workgroup
+  const int RPI = 256 / (HB * LPR);     // keys per instruction (row groups)
+
+  // item order: (head block, sub-group) outermost, then request, then split,
+  // so neighbouring requests (siblings in the tree) share an XCD
+  const int s = (int)(w % a.splits);
+  int64_t rest = w / a.splits;
+  const int r = (int)(rest % a.B);
+  rest /= a.B;
+  const int sub = (int)(rest % a.hg);
+  const int hblk = (int)(rest / a.hg);
+  if (hblk * HB >= a.hkv) return;
+  const int L = min(a.seq_lens[r], a.max_seq_len);
+  int k_begin, k_end, rec, nsplit;
+  if (!split_span(a, r, s, L, k_begin, k_end, rec, nsplit)) return;
+  const int h0 = sub * kMaxG;                   // first q head of this group within a kv group
+  const int nh = min(G, a.G - h0);              // q heads handled here (<= G)
+
+  const int tid = threadIdx.x;
+  const int lr = tid % LPR;                     // lane within row
+  const int hl = (tid / LPR) % HB;              // kv head within the block
+  // row group; wave-uniform (scalar slot loads) when a row group spans whole waves
+  const int ri = (HB * LPR >= 64) ? __builtin_amdgcn_readfirstlane(tid / (HB * LPR)) : tid / (HB * LPR);
+  const int g = hblk * HB + hl;                 // kv head of this lane group
+  const bool gvalid = g < a.hkv;
+  const int gg = gvalid ? g : a.hkv - 1;
+
+  // queries, pre-scaled into the log2 domain
+  float qv[G][VEC];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    const int qh = min(hh, nh - 1);
+    const int64_t qoff = ((int64_t)r * a.hq + (int64_t)gg * a.G + h0 + qh) * D + lr * VEC;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) qv[hh][e] = E::load1(a.q, qoff + e) * a.scale_log2e;
+  }
+  float m[G], l[G], acc[G][VEC];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    m[hh] = -INFINITY;
+    l[hh] = 0.f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[hh][e] = 0.f;
+  }
+
+  const int32_t* row_tab = a.r2t + (int64_t)r * a.ld;
+  const uint32_t P = (uint32_t)min(a.pool_slots, (int64_t)0x7fffffff);
+  const uint32_t slot_bytes = (uint32_t)a.hkv * D * (uint32_t)sizeof(T);
+  const char* kbase = (const char*)a.kp + ((uint64_t)gg * LPR + lr) * 16;
+  const char* vbase = (const char*)a.vp + ((uint64_t)gg * LPR + lr) * 16;
+  const int step = U * RPI;
+
+  // slot indices run one iteration ahead of the K/V gathers that use them
+  int32_t slots[U];
+  auto fetch_slots = [&](int base) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) slots[u] = row_tab[min(base + u * RPI + ri, k_end - 1)];
+  };
+  fetch_slots(k_begin);
+  for (int base = k_begin; base < k_end; base += step) {
+    uint4 kr[U], vr[U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int key = base + u * RPI + ri;       // wave-uniform
+      ok[u] = key < k_end;
+      int32_t slot = slots[u];
+      if ((uint32_t)slot >= P) {
+        if (a.err) rkv::raise_flag(a.err);
+        ok[u] = false;
+        slot = 0;
+      }
+      const uint64_t off = (uint64_t)(uint32_t)slot * slot_bytes;
+      kr[u] = *(const uint4*)(kbase + off);
+      vr[u] = *(const uint4*)(vbase + off);
+    }
+    if (base + step < k_end) fetch_slots(base + step);
+    float sc[U][G];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float kf[VEC];
+      E::unpack(kr[u], kf);
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        float t = 0.f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) t = fmaf(qv[hh][e], kf[e], t);
+        sc[u][hh] = rkv::group_sum<LPR>(t);
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (!ok[u]) sc[u][hh] = -INFINITY;
+        mx = fmaxf(mx, sc[u][hh]);
+      }
+      const float mn = fmaxf(m[hh], mx);
+      const float mref = (mn == -INFINITY) ? 0.f : mn;
+      const float alpha = __builtin_amdgcn_exp2f(m[hh] - mref);
+      l[hh] *= alpha;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[hh][e] *= alpha;
+      m[hh] = mn;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float p = __builtin_amdgcn_exp2f(sc[u][hh] - mref);
+        l[hh] += p;
+        float vf[VEC];
+        E::unpack(vr[u], vf);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[hh][e] = fmaf(p, vf[e], acc[hh][e]);
+      }
+    }
+  }
+
+  // row groups (RPI > 1) merge in LDS: [row group][head in block][G][D + 2]
+  if (RPI > 1) {
+    if (ri > 0) {
+      float* dst = red + (((ri - 1) * HB + hl) * G) * (D + 2);
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) dst[hh * (D + 2) + lr * VEC + e] = acc[hh][e];
+        if (lr == 0) {
+          dst[hh * (D + 2) + D] = m[hh];
+          dst[hh * (D + 2) + D + 1] = l[hh];
+        }
+      }
+    }
+    __syncthreads();
+    if (ri > 0) return;
+    for (int rr = 1; rr < RPI; ++rr) {
+      const float* src = red + (((rr - 1) * HB + hl) * G) * (D + 2);
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        float ab[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) ab[e] = src[hh * (D + 2) + lr * VEC + e];
+        merge_state(m[hh], l[hh], acc[hh], src[hh * (D + 2) + D], src[hh * (D + 2) + D + 1], ab, VEC);
+      }
+    }
+  }
+  if (!gvalid) return;
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    if (hh >= nh) break;
+    const int head = g * a.G + h0 + hh;
+    if (rec < 0) {
+      const float inv = 1.f / l[hh];
+      const int64_t ooff = ((int64_t)r * a.hq + head) * D + lr * VEC;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) E::store1(a.o, ooff + e, acc[hh][e] * inv);
+      if (a.lse && lr == 0) a.lse[(int64_t)r * a.hq + head] = (m[hh] + log2f(l[hh])) * 0.69314718055994531f;
+    } else {
+      float* dst = ws_row(a, D, r, head, rec);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) dst[lr * VEC + e] = acc[hh][e];
+      if (lr == 0) {
+        dst[D] = m[hh];
+        dst[D + 1] = l[hh];
+      }
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void decode_gqa(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) char Vs[2][32 * D * 2];
+  gqa_item<D>(a, rkv::xcd_work_item(blockIdx.x, gridDim.x), Vs);
+}
+
+// Prefix-shared phase 1 in one launch when the tails run on the matrix
+// cores (Hq/Hkv >= 4): blocks [0, shared_blocks) run the shared jobs, the
+// rest the tail splits, one wave per item, so the shared work (a few hundred
+// keys per item) overlaps the long private tails instead of running,
+// latency-bound, before them.  Each range has its own XCD-aware order.  Two
+// waves per SIMD: the register budget of 256 per lane holds CB = 2 at
+// D = 128 (without the hint the compiler takes more and runs one).
+template <int D, int CB>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_cascade_mfma(
+    DecodeArgs a, SharedJobs j, int32_t shared_blocks) {
+  __shared__ __attribute__((aligned(16))) char Vs[2][32 * D * 2];
+  const int b = (int)blockIdx.x;
+  if (b < shared_blocks) {
+    const int64_t w = rkv::xcd_work_item(b, shared_blocks);
+    if (w < (int64_t)j.n_jobs * a.hkv) shared_item<D, CB>(a, j, w, Vs);
+    return;
+  }
+  gqa_item<D>(a, rkv::xcd_work_item(b - shared_blocks, (int64_t)gridDim.x - shared_blocks), Vs);
 }
 
 // Phase 2: one wave per (request, q head); lanes cover D.
@@ -718,7 +761,8 @@ void launch_partial(const DecodeArgs& a, int64_t grid, hipStream_t st) {
   constexpr int LPR = D / Elem<T>::kVec;
   const int rpi = 256 / (a.hb * LPR);
   const size_t lds = rpi > 1 ? (size_t)(rpi - 1) * a.hb * G * (D + 2) * sizeof(float) : 0;
-  hipLaunchKernelGGL((decode_partial<T, D, G, U>), dim3((unsigned)grid), dim3(256), lds, st, a);
+  hipLaunchKernelGGL((decode_partial<T, D, G, U, 0>), dim3((unsigned)grid), dim3(256), lds, st, a, SharedJobs{},
+                     0);
 }
 
 template <typename T, int D>
@@ -746,22 +790,42 @@ void launch_all(const DecodeArgs& a, int64_t grid, hipStream_t st) {
 constexpr int kMaxSharedColumns(int d) { return d == 128 ? 32 : 64; }
 
 template <int D, int CB>
-void launch_shared(const DecodeArgs& a, const SharedJobs& j, hipStream_t st) {
-  int64_t grid = (int64_t)j.n_jobs * a.hkv;
-  grid = (grid + rkv::kXcds - 1) / rkv::kXcds * rkv::kXcds;
-  hipLaunchKernelGGL((decode_shared<D, CB>), dim3((unsigned)grid), dim3(64), 0, st, a, j);
+void launch_cascade_cb(const DecodeArgs& a, const SharedJobs& j, hipStream_t st) {
+  const int64_t items = (int64_t)j.n_jobs * a.hkv;
+  if (a.G >= 4) {
+    // one wave per shared item and per tail item
+    const int64_t sb = (items + rkv::kXcds - 1) / rkv::kXcds * rkv::kXcds;
+    int64_t tb = (int64_t)a.splits * a.B * a.hkv;
+    tb = (tb + rkv::kXcds - 1) / rkv::kXcds * rkv::kXcds;
+    hipLaunchKernelGGL((decode_cascade_mfma<D, CB>), dim3((unsigned)(sb + tb)), dim3(64), 0, st, a, j,
+                       (int32_t)sb);
+    return;
+  }
+  // four shared items per block; tail blocks as the vector kernel's grid
+  const int64_t sb = ((items + 3) / 4 + rkv::kXcds - 1) / rkv::kXcds * rkv::kXcds;
+  int64_t tb = (int64_t)a.splits * a.B * ((a.hkv + a.hb - 1) / a.hb) * a.hg;
+  tb = (tb + rkv::kXcds - 1) / rkv::kXcds * rkv::kXcds;
+  constexpr int LPR = D / 8;
+  const int rpi = 256 / (a.hb * LPR);
+  const int g = a.G < kMaxG ? a.G : kMaxG;
+  auto go = [&](auto gtag) {
+    constexpr int GT = decltype(gtag)::value;
+    constexpr int U = (GT >= 4) ? 2 : (GT >= 2 ? 4 : 8);
+    const size_t lds = rpi > 1 ? (size_t)(rpi - 1) * a.hb * GT * (D + 2) * sizeof(float) : 0;
+    hipLaunchKernelGGL((decode_partial<uint16_t, D, GT, U, CB>), dim3((unsigned)(sb + tb)), dim3(256), lds, st, a,
+                       j, (int32_t)sb);
+  };
+  if (g <= 1) go(std::integral_constant<int, 1>{});
+  else if (g <= 2) go(std::integral_constant<int, 2>{});
+  else go(std::integral_constant<int, 4>{});
 }
 
 template <int D>
 void launch_cascade(const DecodeArgs& a, const SharedJobs& j, int cb, hipStream_t st) {
-  if (j.n_jobs > 0) {
-    if (cb <= 1) launch_shared<D, 1>(a, j, st);
-    else if (cb <= 2 || D == 128) launch_shared<D, 2>(a, j, st);
-    else if constexpr (D == 64) launch_shared<D, 4>(a, j, st);
-  }
-  int64_t grid = (int64_t)a.splits * a.B * ((a.hkv + a.hb - 1) / a.hb) * a.hg;
-  grid = (grid + rkv::kXcds - 1) / rkv::kXcds * rkv::kXcds;
-  launch_all<uint16_t, D>(a, grid, st);
+  if (cb <= 1) launch_cascade_cb<D, 1>(a, j, st);
+  else if (cb <= 2 || D == 128) launch_cascade_cb<D, 2>(a, j, st);
+  else if constexpr (D == 64) launch_cascade_cb<D, 4>(a, j, st);
+  hipLaunchKernelGGL((decode_merge<uint16_t, D>), dim3((unsigned)((int64_t)a.B * a.hq)), dim3(64), 0, st, a);
 }
 
 // kv heads per workgroup of the vector kernel (a power of two, at most 4):
@@ -902,7 +966,7 @@ extern "C" int rkv_attn_decode_cascade(const void* q, const void* k_pool, const 
   j.n_jobs = (int32_t)n_jobs;
   j.max_members = max_members;
   const int cb = (max_members * G + 15) / 16;
-  if ((int64_t)n_jobs * hkv > 0x7fffffff || (int64_t)tail_splits * B * hkv > 0x7fffffff)
+  if ((int64_t)n_jobs * hkv + (int64_t)tail_splits * B * hkv + 64 > 0x7fffffff)
     return rkv::fail(RKV_ENOTSUP, "rkv_attn_decode_cascade: grid too large");
   hipStream_t st = (hipStream_t)stream;
   if (d == 128) launch_cascade<128>(a, j, cb, st); else launch_cascade<64>(a, j, cb, st);

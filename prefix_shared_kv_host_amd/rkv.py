@@ -383,11 +383,13 @@ def cascade_plan(req_to_token, seq_lens, seg_chunk=256, tail_chunk=768, min_keys
                               int(tail_chunk), int(min_keys), int(max_members), perm.ctypes.data_as(c_i32p),
                               rec.ctypes.data_as(c_i32p), tb.ctypes.data_as(c_i32p), jobs, cap,
                               ctypes.byref(n_jobs), ctypes.byref(tail))
-    code = lib().rkv_cascade_plan(*args(None, 0))
-    if code not in (OK, ENOSPC):
-        _check(code)
-    jobs = np.empty((max(n_jobs.value, 1), 5), dtype=np.int32)
-    _check(lib().rkv_cascade_plan(*args(jobs.ctypes.data_as(c_i32p), n_jobs.value)))
+    # one call with a generous capacity; a second only when it was too small
+    jobs = np.empty((max(64, 8 * B), 5), dtype=np.int32)
+    code = lib().rkv_cascade_plan(*args(jobs.ctypes.data_as(c_i32p), jobs.shape[0]))
+    if code == ENOSPC:
+        jobs = np.empty((n_jobs.value, 5), dtype=np.int32)
+        code = lib().rkv_cascade_plan(*args(jobs.ctypes.data_as(c_i32p), n_jobs.value))
+    _check(code)
     return CascadePlan(perm[:B], rec, tb[:B], jobs[: n_jobs.value], tail.value, max_members, tail_chunk)
 
 

@@ -165,6 +165,49 @@ print("CLEAN-OK")
 """
 
 
+_DEBUG_CASCADE_SCRIPT = r"""
+import sys, numpy as np, torch
+sys.path.insert(0, sys.argv[1])
+from prefix_shared_kv_host_amd import rkv
+P, hkv, d, hq = 256, 2, 128, 2
+kp = torch.zeros(P, hkv, d, dtype=torch.bfloat16, device="cuda")
+vp = torch.zeros_like(kp)
+# three requests share slots 0..39, then private tails
+L = np.array([60, 55, 70], dtype=np.int32)
+r2t = np.full((3, 80), -1, dtype=np.int32)
+nxt = 40
+for r in range(3):
+    r2t[r, :40] = np.arange(40)
+    r2t[r, 40:L[r]] = np.arange(nxt, nxt + L[r] - 40); nxt += L[r] - 40
+q = torch.zeros(3, hq, d, dtype=torch.bfloat16, device="cuda")
+o = torch.empty_like(q)
+sl = torch.from_numpy(L).cuda()
+
+def run(table, plan):
+    plan.to("cuda")
+    ws = torch.empty(rkv.attn_decode_cascade_workspace_bytes(plan.n_records, hq, d) // 4 + 1, device="cuda")
+    try:
+        rkv.attn_decode_cascade(q, kp, vp, o, torch.from_numpy(table).cuda(), sl, 80, plan, ws)
+        torch.cuda.synchronize()
+        print("NO-ERROR")
+    except rkv.RkvError as e:
+        print("CODE", e.code)
+
+base = rkv.cascade_plan(r2t, L, 16, 32, 8, 8)
+assert base.n_jobs >= 1
+bad_slot = r2t.copy(); bad_slot[:, 20] = 10**6          # inside the shared run (every row)
+run(bad_slot, base)
+p = rkv.cascade_plan(r2t, L, 16, 32, 8, 8); p.jobs[0, 2] = 2; p.jobs[0, 3] = 2   # members past B
+run(r2t, p)
+p = rkv.cascade_plan(r2t, L, 16, 32, 8, 8); p.jobs[0, 4] = 100                 # record past the request's
+run(r2t, p)
+p = rkv.cascade_plan(r2t, L, 16, 32, 8, 8); p.tail_begin[2] = 70               # empty tail
+run(r2t, p)
+run(r2t, rkv.cascade_plan(r2t, L, 16, 32, 8, 8))
+print("CLEAN-OK")
+"""
+
+
 @pytest.mark.parametrize("script", [_DEBUG_SCRIPT, _DEBUG_EXTEND_SCRIPT], ids=["decode", "extend"])
 def test_debug_mode_flags_out_of_range_slot(script):
     env = dict(os.environ, RKV_DEBUG="1")
@@ -172,3 +215,15 @@ def test_debug_mode_flags_out_of_range_slot(script):
                        text=True, timeout=180)
     G.log(p.stdout + p.stderr[-2000:])
     assert "CODE -1" in p.stdout and "CLEAN-OK" in p.stdout
+
+
+def test_debug_mode_flags_cascade_plan_that_does_not_fit():
+    """An out-of-range slot in a shared run, a job whose members run past the
+    batch, a record past the request's range and an empty tail are each
+    caught by the kernels' checks (RKV_EINVAL under RKV_DEBUG=1, nothing
+    indexed out of range); the unmodified plan then runs clean."""
+    env = dict(os.environ, RKV_DEBUG="1")
+    p = subprocess.run([sys.executable, "-c", _DEBUG_CASCADE_SCRIPT, ROOT], env=env, capture_output=True,
+                       text=True, timeout=180)
+    G.log(p.stdout + p.stderr[-2000:])
+    assert p.stdout.split() == ["CODE", "-1"] * 4 + ["NO-ERROR", "CLEAN-OK"], p.stdout + p.stderr[-2000:]
