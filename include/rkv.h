@@ -321,6 +321,64 @@ int rkv_attn_decode_cascade(const void* q, const void* k_pool, const void* v_poo
                             int32_t max_members, int32_t tail_chunk, int32_t tail_splits, int64_t n_records,
                             void* workspace, size_t ws_bytes, int64_t pool_slots, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Sampling penalties over the running requests (the sampling page,
+ * sglang-zh.llamafactory.cn, "sampling_params": the Penalties block defines
+ * frequency_penalty, presence_penalty, repetition_penalty and
+ * min_new_tokens; its section on the performance implications of penalties
+ * puts them on the GPU for the whole batch, with state of size vocab x
+ * running requests).  Formulas (the page gives intent and ranges only):
+ *   for every token of the prompt or the output: x = x > 0 ? x / r : x * r;
+ *   for every token of the output: x = x - f * count - p;
+ *   while out_len < min_new_tokens: x = -inf for the request's stop ids
+ *   (its EOS and stop_token_ids), after the two steps above.
+ * fp32 arithmetic (x / r correctly rounded, then one fma for -f*count and
+ * one subtraction); bf16 logits are read exactly and written rounded to
+ * nearest even.
+ *
+ * State, per request slot (device memory owned by the caller; slots index
+ * rows, so requests can come and go):
+ *   counts [n_slots, vocab] int32: bits 0..30 = times the token occurs in
+ *     the output so far (saturating), bit 31 = it occurs in the prompt;
+ *   seen [n_slots, cap] int32 and seen_len [n_slots]: the distinct tokens of
+ *     prompt and output, each once, in unspecified order; cap must be at
+ *     least the request's distinct prompt tokens plus its output length;
+ *   out_len [n_slots]: output tokens so far.
+ * Rows, token ids and stop ids are range-checked in the kernels: an entry out
+ * of range (or a full seen list) is skipped, and with RKV_DEBUG=1 the call
+ * returns RKV_EINVAL after a stream synchronization.
+ * ------------------------------------------------------------------------ */
+
+/* Admits n requests: for request i, slot rows[i] is reset (counts row zero,
+ * out_len 0) and its prompt prompt_ids[prompt_indptr[i] ..
+ * prompt_indptr[i+1]) (device int32, n+1 offsets) is marked in bit 31 and
+ * listed in seen.  rows must be distinct.  n = 0 is a no-op. */
+int rkv_penalty_admit(int32_t* counts, int32_t* seen, int32_t* seen_len, int32_t* out_len, int32_t n_slots,
+                      int32_t vocab, int32_t cap, int32_t n, const int32_t* rows, const int32_t* prompt_indptr,
+                      const int32_t* prompt_ids, void* stream);
+
+/* Records one output token per running request: for b in [0, B), tokens[b]
+ * is appended to slot rows[b] (count + 1, listed in seen if new, out_len +
+ * 1).  rows must be distinct.  Call it after sampling, before the next
+ * apply.  B = 0 is a no-op. */
+int rkv_penalty_accumulate(int32_t* counts, int32_t* seen, int32_t* seen_len, int32_t* out_len, int32_t n_slots,
+                           int32_t vocab, int32_t cap, int32_t B, const int32_t* rows, const int32_t* tokens,
+                           void* stream);
+
+/* Applies the penalties in place to logits [B, ld] (row b belongs to slot
+ * rows[b]; dtype RKV_F32 or RKV_BF16; ld >= vocab; only the first vocab
+ * entries of a row are read or written).  Per batch entry b (device
+ * arrays): freq[b], pres[b], rep[b] (float), min_new[b] (int32), stop ids
+ * stop_ids[stop_indptr[b] .. stop_indptr[b+1]) (stop_ids may be NULL when
+ * every list is empty).  Only the logits of listed tokens and, while
+ * masking, the stop ids are touched: O(prompt + output) entries per
+ * request, not O(vocab).  B = 0 is a no-op. */
+int rkv_penalty_apply(void* logits, int64_t ld, int32_t dtype, int32_t B, const int32_t* rows,
+                      const int32_t* counts, const int32_t* seen, const int32_t* seen_len, const int32_t* out_len,
+                      int32_t n_slots, int32_t vocab, int32_t cap, const float* freq, const float* pres,
+                      const float* rep, const int32_t* min_new, const int32_t* stop_indptr, const int32_t* stop_ids,
+                      void* stream);
+
 #ifdef __cplusplus
 }
 #endif

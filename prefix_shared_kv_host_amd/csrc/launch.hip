@@ -43,7 +43,7 @@ int finish_launch(const char* what, hipStream_t stream, int* flag) {
   if (h) {
     int zero = 0;
     (void)hipMemcpy(flag, &zero, sizeof(int), hipMemcpyHostToDevice);
-    return fail(RKV_EINVAL, std::string(what) + ": a slot index was outside [0, pool_slots)");
+    return fail(RKV_EINVAL, std::string(what) + ": an index (slot, token, request or plan entry) was out of range");
   }
   return RKV_OK;
 }

@@ -30,7 +30,8 @@ EXPORTS = (
     "rkv_free", "rkv_stats", "rkv_radix_serialize", "rkv_free_list", "rkv_batch_prepare",
     "rkv_batch_commit", "rkv_kv_scatter", "rkv_attn_extend", "rkv_attn_decode_workspace_bytes",
     "rkv_attn_decode", "rkv_radix_peek", "rkv_schedule", "rkv_cascade_plan",
-    "rkv_attn_decode_cascade_workspace_bytes", "rkv_attn_decode_cascade",
+    "rkv_attn_decode_cascade_workspace_bytes", "rkv_attn_decode_cascade", "rkv_penalty_admit",
+    "rkv_penalty_accumulate", "rkv_penalty_apply",
 )
 
 
@@ -88,6 +89,10 @@ def lib():
         "rkv_attn_decode_cascade": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32, _i32, _i32,
                                                    _i32, _i32, _f32, _i32, _vp, _vp, _vp, _vp, _i64, _i32,
                                                    _i32, _i32, _i64, _vp, _sz, _i64, _vp]),
+        "rkv_penalty_admit": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
+        "rkv_penalty_accumulate": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
+        "rkv_penalty_apply": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp,
+                                             _vp, _vp, _vp, _vp, _vp, _vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -415,3 +420,45 @@ def attn_decode_cascade(q, k_pool, v_pool, o, req_to_token, seq_lens, max_seq_le
         scale, _dtype_code(q), _ptr(dv["perm"]), _ptr(dv["rec_indptr"]), _ptr(dv["tail_begin"]),
         _ptr(dv["jobs"]) if plan.n_jobs else None, plan.n_jobs, plan.max_members, plan.tail_chunk,
         plan.tail_splits, plan.n_records, _ptr(workspace), int(ws_bytes), int(P), _stream(stream)))
+
+
+class PenaltyState:
+    """Device state of the sampling penalties for n_slots request slots over
+    a vocabulary (rkv_penalty_*): counts [n_slots, vocab], seen [n_slots,
+    cap], seen_len and out_len [n_slots], all int32 torch tensors."""
+
+    def __init__(self, n_slots, vocab, cap, device="cuda"):
+        import torch
+        self.n_slots, self.vocab, self.cap = int(n_slots), int(vocab), int(cap)
+        self.counts = torch.zeros(n_slots, vocab, dtype=torch.int32, device=device)
+        self.seen = torch.zeros(n_slots, cap, dtype=torch.int32, device=device)
+        self.seen_len = torch.zeros(n_slots, dtype=torch.int32, device=device)
+        self.out_len = torch.zeros(n_slots, dtype=torch.int32, device=device)
+
+    def _st(self):
+        return (_ptr(self.counts), _ptr(self.seen), _ptr(self.seen_len), _ptr(self.out_len), self.n_slots,
+                self.vocab, self.cap)
+
+    def admit(self, rows, prompt_indptr, prompt_ids, stream=None):
+        """rows [n], prompt_indptr [n+1], prompt_ids: device int32 tensors."""
+        _need_cuda(rows, prompt_indptr, prompt_ids)
+        return _check(lib().rkv_penalty_admit(*self._st(), int(rows.shape[0]), _ptr(rows), _ptr(prompt_indptr),
+                                              _ptr(prompt_ids), _stream(stream)))
+
+    def accumulate(self, rows, tokens, stream=None):
+        """One output token per running request: rows [B], tokens [B] (device int32)."""
+        _need_cuda(rows, tokens)
+        return _check(lib().rkv_penalty_accumulate(*self._st(), int(rows.shape[0]), _ptr(rows), _ptr(tokens),
+                                                   _stream(stream)))
+
+    def apply(self, logits, rows, freq, pres, rep, min_new, stop_indptr, stop_ids, stream=None):
+        """Penalizes logits [B, >= vocab] (fp32 or bf16) in place; per-entry
+        device arrays freq, pres, rep (float32), min_new (int32), stop lists
+        as CSR (stop_indptr [B+1], stop_ids)."""
+        _need_cuda(logits, rows, freq, pres, rep, min_new, stop_indptr, stop_ids)
+        B = int(rows.shape[0])
+        return _check(lib().rkv_penalty_apply(
+            _ptr(logits), int(logits.shape[1]), _dtype_code(logits), B, _ptr(rows), _ptr(self.counts),
+            _ptr(self.seen), _ptr(self.seen_len), _ptr(self.out_len), self.n_slots, self.vocab, self.cap,
+            _ptr(freq), _ptr(pres), _ptr(rep), _ptr(min_new), _ptr(stop_indptr),
+            _ptr(stop_ids) if stop_ids is not None and stop_ids.numel() else None, _stream(stream)))
