@@ -271,6 +271,71 @@ def chat_pipeline(name):
     return out
 
 
+def sampling_penalties(steps=64, warmup=8):
+    """Batched sampling penalties on the decode loop: 256 running requests,
+    vocabulary 32000 (Llama-7B), 256-token prompts, with the sampling page's
+    "all penalties" benchmark settings (frequency 1.1, presence 1.1,
+    repetition 0.1, min_new_tokens 5, EOS id 2).  Each step applies the
+    penalties to the fp32 logits [256, 32000] in place and records one
+    seeded output token per request; HIP events on the launch stream."""
+    import torch
+    from prefix_shared_kv_host_amd import rkv
+    B, V, P = 256, 32000, 256
+    rng = np.random.default_rng(61)
+    st = rkv.PenaltyState(B, V, P + warmup + steps + 8)
+    rows = torch.arange(B, dtype=torch.int32, device="cuda")
+    prompts = (rng.zipf(1.2, (B, P)) % V).astype(np.int32)
+    indptr = torch.arange(0, B * P + 1, P, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    pids = torch.from_numpy(prompts.reshape(-1)).cuda()
+    st.admit(rows, indptr, pids)                # first launch loads the code object
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    st.admit(rows, indptr, pids)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    admit_us = ev[0].elapsed_time(ev[1]) * 1e3
+    # output tokens: half repeat a prompt or earlier token, half fresh
+    toks = np.where(rng.random((warmup + steps, B)) < 0.5, prompts[np.arange(B), rng.integers(0, P, (warmup + steps, B))],
+                    rng.integers(0, V, (warmup + steps, B))).astype(np.int32)
+    toks = torch.from_numpy(toks).cuda()
+    f32 = lambda v: torch.full((B,), v, dtype=torch.float32, device="cuda")
+    freq, pres, rep = f32(1.1), f32(1.1), f32(0.1)
+    min_new = torch.full((B,), 5, dtype=torch.int32, device="cuda")
+    stop_indptr = torch.arange(B + 1, dtype=torch.int32, device="cuda")
+    stop_ids = torch.full((B,), 2, dtype=torch.int32, device="cuda")
+    logits = torch.randn(B, V, device="cuda")
+    # decode step = one launch: record the previous token, then penalize
+    ap, sep = [], []
+    for i in range(warmup + steps):
+        ev[0].record(stream)
+        st.apply(logits, rows, freq, pres, rep, min_new, stop_indptr, stop_ids, new_tokens=toks[i])
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        if i >= warmup:
+            ap.append(ev[0].elapsed_time(ev[1]))
+    seen = int(st.seen_len.sum().item())
+    # the same step as two launches (accumulate, then apply), for comparison
+    for i in range(warmup + steps):
+        ev[0].record(stream)
+        st.accumulate(rows, toks[i])
+        st.apply(logits, rows, freq, pres, rep, min_new, stop_indptr, stop_ids)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        if i >= warmup:
+            sep.append(ev[0].elapsed_time(ev[1]))
+    step_us, sep_us = float(np.mean(ap)) * 1e3, float(np.mean(sep)) * 1e3
+    moved = float(seen * 16 + B * 4 * 10)       # per listed token: list, count, logit read and write
+    dense = float(B * V * 12)                   # a full-vocabulary sweep: logits read + write, counts read
+    return dict(workload="256 running requests x vocab 32000, 256-token prompts, freq 1.1 / presence 1.1 / "
+                         "repetition 0.1 / min_new_tokens 5, fp32 logits",
+                step_us=step_us, step_us_two_launches=sep_us, admit_us=admit_us,
+                listed_tokens_at_end=seen, step_bytes_at_end=moved,
+                dense_sweep_bytes=dense, dense_sweep_us_at_hbm_peak=dense / (PEAK_HBM_GBS * 1e3),
+                requests_per_s=B / (step_us * 1e-6))
+
+
 def queue_orders():
     """Cache hit rate of the multi-turn chat trace under a serving queue (a
     session's next turn is runnable once its previous turn ran; <= 64 turns a
@@ -553,6 +618,7 @@ def main():
     out["gqa_llama70b"] = gqa_halves(max(5, args.steps // 2), 3)
     out["chat_pipeline"] = [chat_pipeline("c5"), chat_pipeline("c5e")]
     out["cache_aware_scheduling"] = queue_orders()
+    out["sampling_penalties"] = sampling_penalties()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out))

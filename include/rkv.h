@@ -370,13 +370,16 @@ int rkv_penalty_accumulate(int32_t* counts, int32_t* seen, int32_t* seen_len, in
  * entries of a row are read or written).  Per batch entry b (device
  * arrays): freq[b], pres[b], rep[b] (float), min_new[b] (int32), stop ids
  * stop_ids[stop_indptr[b] .. stop_indptr[b+1]) (stop_ids may be NULL when
- * every list is empty).  Only the logits of listed tokens and, while
- * masking, the stop ids are touched: O(prompt + output) entries per
- * request, not O(vocab).  B = 0 is a no-op. */
-int rkv_penalty_apply(void* logits, int64_t ld, int32_t dtype, int32_t B, const int32_t* rows,
-                      const int32_t* counts, const int32_t* seen, const int32_t* seen_len, const int32_t* out_len,
-                      int32_t n_slots, int32_t vocab, int32_t cap, const float* freq, const float* pres,
-                      const float* rep, const int32_t* min_new, const int32_t* stop_indptr, const int32_t* stop_ids,
+ * every list is empty).  new_tokens (nullable, [B]): when given, each
+ * request's previous output token is first recorded exactly as
+ * rkv_penalty_accumulate does, in the same launch (one launch per decode
+ * step).  Only the logits of listed tokens and, while masking, the stop ids
+ * are touched: O(prompt + output) entries per request, not O(vocab).
+ * rows must be distinct.  B = 0 is a no-op. */
+int rkv_penalty_apply(void* logits, int64_t ld, int32_t dtype, int32_t B, const int32_t* rows, int32_t* counts,
+                      int32_t* seen, int32_t* seen_len, int32_t* out_len, int32_t n_slots, int32_t vocab,
+                      int32_t cap, const float* freq, const float* pres, const float* rep, const int32_t* min_new,
+                      const int32_t* stop_indptr, const int32_t* stop_ids, const int32_t* new_tokens,
                       void* stream);
 
 #ifdef __cplusplus

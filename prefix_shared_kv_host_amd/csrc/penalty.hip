@@ -58,7 +58,9 @@ __global__ __launch_bounds__(256) void penalty_admit_kernel(int32_t* __restrict_
   uint32_t* crow = (uint32_t*)counts + (int64_t)row * vocab;
   for (int v = threadIdx.x; v < vocab; v += blockDim.x) crow[v] = 0u;
   if (threadIdx.x == 0) n_listed = 0;
-  __threadfence();     // the zeros reach L2 before any lane's atomic OR there
+  // the barrier's work-group release waits for the zero stores to complete
+  // in L2, where the atomic ORs below execute (a device-scope fence would
+  // write back the whole L2 of this XCD and is not needed)
   __syncthreads();
   const int p0 = prompt_indptr[i], p1 = prompt_indptr[i + 1];
   int32_t* srow = seen + (int64_t)row * cap;
@@ -82,9 +84,31 @@ __global__ __launch_bounds__(256) void penalty_admit_kernel(int32_t* __restrict_
   }
 }
 
-// One lane per running request: its new output token is counted, listed if
-// the request has not seen it before, and the output length grows by one.
-// Rows are distinct within a call, so no two lanes touch the same state.
+// Records output token t of the request in slot `row` (row already checked):
+// counted, listed if the request has not seen it before, output length + 1.
+__device__ __forceinline__ void record_token(int32_t* counts, int32_t* seen, int32_t* seen_len, int32_t* out_len,
+                                             int32_t vocab, int32_t cap, int row, int t, int* err) {
+  if (t < 0 || t >= vocab) {
+    if (err) rkv::raise_flag(err);
+    return;
+  }
+  uint32_t* w = (uint32_t*)counts + (int64_t)row * vocab + t;
+  const uint32_t c = *w;
+  const int n = seen_len[row];
+  if ((c & kCountMask) != kCountMask) *w = c + 1u;
+  if (c == 0u) {
+    if (n < cap) {
+      seen[(int64_t)row * cap + n] = t;
+      seen_len[row] = n + 1;
+    } else if (err) {
+      rkv::raise_flag(err);
+    }
+  }
+  out_len[row] += 1;
+}
+
+// One lane per running request.  Rows are distinct within a call, so no two
+// lanes touch the same state.
 __global__ __launch_bounds__(256) void penalty_accumulate_kernel(int32_t* __restrict__ counts,
                                                                 int32_t* __restrict__ seen,
                                                                 int32_t* __restrict__ seen_len,
@@ -94,24 +118,12 @@ __global__ __launch_bounds__(256) void penalty_accumulate_kernel(int32_t* __rest
                                                                 const int32_t* __restrict__ tokens, int* err) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= B) return;
-  const int row = rows[b], t = tokens[b];
-  if (row < 0 || row >= n_slots || t < 0 || t >= vocab) {
+  const int row = rows[b];
+  if (row < 0 || row >= n_slots) {
     if (err) rkv::raise_flag(err);
     return;
   }
-  uint32_t* w = (uint32_t*)counts + (int64_t)row * vocab + t;
-  const uint32_t c = *w;
-  if ((c & kCountMask) != kCountMask) *w = c + 1u;
-  if (c == 0u) {
-    const int n = seen_len[row];
-    if (n < cap) {
-      seen[(int64_t)row * cap + n] = t;
-      seen_len[row] = n + 1;
-    } else if (err) {
-      rkv::raise_flag(err);
-    }
-  }
-  out_len[row] += 1;
+  record_token(counts, seen, seen_len, out_len, vocab, cap, row, tokens[b], err);
 }
 
 template <typename T>
@@ -127,23 +139,25 @@ struct Logit<uint16_t> {
   __device__ static void store(void* p, int64_t i, float v) { ((uint16_t*)p)[i] = rkv::f32_to_bf16(v); }
 };
 
-// One workgroup per batch entry b (state row rows[b], logits row b).  Every
-// listed token is penalized in place; then, after a barrier (so a stop token
-// that is also listed ends at -inf), the stop mask.  Each lane loads its
-// listed tokens, their counts and their logits in batches of kPer before
-// computing, so the three dependent gathers overlap across entries.
-template <typename T>
+// One workgroup per batch entry b (state row rows[b], logits row b).  With
+// RECORD, lane 0 first records new_tokens[b] (the token sampled at the
+// previous step), so one launch per decode step both updates the state and
+// penalizes.  Every listed token is then penalized in place; after a barrier
+// (so a stop token that is also listed ends at -inf) comes the stop mask.
+// The first kPer list entries of every lane are loaded together with the
+// list length (the row stride cap bounds them), and then their counts and
+// logits together, so the dependent gathers overlap.
+template <typename T, bool RECORD>
 __global__ __launch_bounds__(256) void penalty_apply_kernel(void* __restrict__ logits, int64_t ld, int32_t B,
-                                                           const int32_t* __restrict__ rows,
-                                                           const int32_t* __restrict__ counts,
-                                                           const int32_t* __restrict__ seen,
-                                                           const int32_t* __restrict__ seen_len,
-                                                           const int32_t* __restrict__ out_len, int32_t n_slots,
-                                                           int32_t vocab, int32_t cap, const float* __restrict__ freq,
+                                                           const int32_t* __restrict__ rows, int32_t* counts,
+                                                           int32_t* seen, int32_t* seen_len, int32_t* out_len,
+                                                           int32_t n_slots, int32_t vocab, int32_t cap,
+                                                           const float* __restrict__ freq,
                                                            const float* __restrict__ pres, const float* __restrict__ rep,
                                                            const int32_t* __restrict__ min_new,
                                                            const int32_t* __restrict__ stop_indptr,
-                                                           const int32_t* __restrict__ stop_ids, int* err) {
+                                                           const int32_t* __restrict__ stop_ids,
+                                                           const int32_t* __restrict__ new_tokens, int* err) {
   using L = Logit<T>;
   constexpr int kPer = 4;
   const int b = blockIdx.x;
@@ -152,19 +166,30 @@ __global__ __launch_bounds__(256) void penalty_apply_kernel(void* __restrict__ l
     if (threadIdx.x == 0 && err) rkv::raise_flag(err);
     return;
   }
+  if constexpr (RECORD) {
+    // the record and its readers are in this work-group: the barrier's
+    // work-group release and acquire make the record visible to them
+    if (threadIdx.x == 0) record_token(counts, seen, seen_len, out_len, vocab, cap, row, new_tokens[b], err);
+    __syncthreads();
+  }
   const float f = freq[b], p = pres[b], r = rep[b];
-  const int n = min(seen_len[row], cap);
   const uint32_t* crow = (const uint32_t*)counts + (int64_t)row * vocab;
   const int32_t* srow = seen + (int64_t)row * cap;
   const int64_t lbase = (int64_t)b * ld;
-  for (int k0 = 0; k0 < n; k0 += kPer * blockDim.x) {
+  const int n = min(seen_len[row], cap);
+  for (int k0 = 0; k0 == 0 || k0 < n; k0 += kPer * blockDim.x) {
     int t[kPer];
     uint32_t c[kPer];
     float x[kPer];
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int k = k0 + u * blockDim.x + threadIdx.x;
-      t[u] = k < n ? srow[k] : -1;
+      t[u] = k < cap ? srow[k] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int k = k0 + u * blockDim.x + threadIdx.x;
+      if (k >= n) t[u] = -1;
       if (t[u] >= vocab) {
         if (err) rkv::raise_flag(err);
         t[u] = -1;
@@ -237,10 +262,10 @@ extern "C" int rkv_penalty_accumulate(int32_t* counts, int32_t* seen, int32_t* s
 }
 
 extern "C" int rkv_penalty_apply(void* logits, int64_t ld, int32_t dtype, int32_t B, const int32_t* rows,
-                                 const int32_t* counts, const int32_t* seen, const int32_t* seen_len,
-                                 const int32_t* out_len, int32_t n_slots, int32_t vocab, int32_t cap,
-                                 const float* freq, const float* pres, const float* rep, const int32_t* min_new,
-                                 const int32_t* stop_indptr, const int32_t* stop_ids, void* stream) {
+                                 int32_t* counts, int32_t* seen, int32_t* seen_len, int32_t* out_len,
+                                 int32_t n_slots, int32_t vocab, int32_t cap, const float* freq, const float* pres,
+                                 const float* rep, const int32_t* min_new, const int32_t* stop_indptr,
+                                 const int32_t* stop_ids, const int32_t* new_tokens, void* stream) {
   rkv::clear_error();
   if (n_slots < 1 || vocab < 1 || cap < 1 || B < 0 || ld < vocab)
     return rkv::fail(RKV_EINVAL, "rkv_penalty_apply: bad sizes");
@@ -252,13 +277,14 @@ extern "C" int rkv_penalty_apply(void* logits, int64_t ld, int32_t dtype, int32_
   int* flag = nullptr;
   if (int rc = rkv::debug_flag(&flag)) return rc;
   hipStream_t st = (hipStream_t)stream;
-  if (dtype == RKV_F32)
-    hipLaunchKernelGGL(penalty_apply_kernel<float>, dim3((unsigned)B), dim3(256), 0, st, logits, ld, B, rows, counts,
-                       seen, seen_len, out_len, n_slots, vocab, cap, freq, pres, rep, min_new, stop_indptr, stop_ids,
-                       flag);
-  else
-    hipLaunchKernelGGL(penalty_apply_kernel<uint16_t>, dim3((unsigned)B), dim3(256), 0, st, logits, ld, B, rows,
-                       counts, seen, seen_len, out_len, n_slots, vocab, cap, freq, pres, rep, min_new, stop_indptr,
-                       stop_ids, flag);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3((unsigned)B), dim3(256), 0, st, logits, ld, B, rows, counts, seen, seen_len,
+                       out_len, n_slots, vocab, cap, freq, pres, rep, min_new, stop_indptr, stop_ids, new_tokens, flag);
+  };
+  if (dtype == RKV_F32) {
+    if (new_tokens) go(penalty_apply_kernel<float, true>); else go(penalty_apply_kernel<float, false>);
+  } else {
+    if (new_tokens) go(penalty_apply_kernel<uint16_t, true>); else go(penalty_apply_kernel<uint16_t, false>);
+  }
   return rkv::finish_launch("rkv_penalty_apply", st, flag);
 }

@@ -92,7 +92,7 @@ def lib():
         "rkv_penalty_admit": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
         "rkv_penalty_accumulate": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
         "rkv_penalty_apply": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp,
-                                             _vp, _vp, _vp, _vp, _vp, _vp]),
+                                             _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -451,14 +451,17 @@ class PenaltyState:
         return _check(lib().rkv_penalty_accumulate(*self._st(), int(rows.shape[0]), _ptr(rows), _ptr(tokens),
                                                    _stream(stream)))
 
-    def apply(self, logits, rows, freq, pres, rep, min_new, stop_indptr, stop_ids, stream=None):
+    def apply(self, logits, rows, freq, pres, rep, min_new, stop_indptr, stop_ids, new_tokens=None, stream=None):
         """Penalizes logits [B, >= vocab] (fp32 or bf16) in place; per-entry
         device arrays freq, pres, rep (float32), min_new (int32), stop lists
-        as CSR (stop_indptr [B+1], stop_ids)."""
-        _need_cuda(logits, rows, freq, pres, rep, min_new, stop_indptr, stop_ids)
+        as CSR (stop_indptr [B+1], stop_ids).  new_tokens [B] (optional):
+        each request's previous output token, recorded first in the same
+        launch."""
+        _need_cuda(logits, rows, freq, pres, rep, min_new, stop_indptr, stop_ids, new_tokens)
         B = int(rows.shape[0])
         return _check(lib().rkv_penalty_apply(
             _ptr(logits), int(logits.shape[1]), _dtype_code(logits), B, _ptr(rows), _ptr(self.counts),
             _ptr(self.seen), _ptr(self.seen_len), _ptr(self.out_len), self.n_slots, self.vocab, self.cap,
             _ptr(freq), _ptr(pres), _ptr(rep), _ptr(min_new), _ptr(stop_indptr),
-            _ptr(stop_ids) if stop_ids is not None and stop_ids.numel() else None, _stream(stream)))
+            _ptr(stop_ids) if stop_ids is not None and stop_ids.numel() else None, _ptr(new_tokens),
+            _stream(stream)))

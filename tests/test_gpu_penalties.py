@@ -2,7 +2,8 @@
 apply) against the float64 oracle (oracle/penalties.py), over a simulated
 decode loop: requests are admitted into scattered slots with their prompts;
 every step penalizes fresh seeded logits, is compared with the oracle, and
-then records one seeded output token per request.
+then records one seeded output token per request, on alternate steps by
+rkv_penalty_accumulate and by the next rkv_penalty_apply itself.
 
 Tolerance (derived from the arithmetic): the kernel divides once (correctly
 rounded), then one fma and one subtraction in fp32, so
@@ -106,14 +107,23 @@ def test_penalty_decode_loop(dtype, V, B, steps):
     args = dict(freq=dev(f, torch.float32), pres=dev(p, torch.float32), rep=dev(r, torch.float32),
                 min_new=dev(m), stop_indptr=dev(sp), stop_ids=dev(sf))
     ld = V + 37
+    pending = None
     for step in range(steps):
         full = torch.randn(B, ld, generator=torch.Generator().manual_seed(step), dtype=torch.float32) * 4
         full[0, :7] = 0.0                                              # zero logits, r = 0 path
         lg = full.to(dtype).cuda()
         before = lg.float().cpu().numpy()[:, :V].astype(np.float64)
         pad_before = lg.float().cpu().numpy()[:, V:]
-        st.apply(lg, dev(slot_of), **args)
+        if pending is not None:
+            # the previous step's tokens are recorded inside this launch
+            for i in range(B):
+                outputs[i].append(pending[i])
+            st.apply(lg, dev(slot_of), new_tokens=dev(pending), **args)
+            pending = None
+        else:
+            st.apply(lg, dev(slot_of), **args)
         torch.cuda.synchronize()
+        _check_state(st, slot_of, prompts, outputs, V)
         after = lg.float().cpu().numpy()
         assert np.array_equal(after[:, V:], pad_before, equal_nan=True)   # past vocab: untouched
         _check_step(before, after[:, :V].astype(np.float64), prompts, outputs, f, p, r, m, stops, dtype, V)
@@ -122,11 +132,14 @@ def test_penalty_decode_loop(dtype, V, B, steps):
         for i in range(B):
             pool = prompts[i] + outputs[i]
             nxt.append(int(rng.choice(pool)) if pool and rng.random() < 0.6 else int(rng.integers(0, V)))
-        st.accumulate(dev(slot_of), dev(nxt))
-        for i in range(B):
-            outputs[i].append(nxt[i])
-        torch.cuda.synchronize()
-        _check_state(st, slot_of, prompts, outputs, V)
+        if step % 2 == 0:
+            st.accumulate(dev(slot_of), dev(nxt))
+            for i in range(B):
+                outputs[i].append(nxt[i])
+            torch.cuda.synchronize()
+            _check_state(st, slot_of, prompts, outputs, V)
+        else:
+            pending = nxt
     G.log(f"penalties {dtype} V={V} B={B}: {steps} steps checked")
 
 
