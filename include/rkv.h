@@ -107,6 +107,17 @@ int rkv_radix_peek(const rkv_tree* t, const int32_t* tok, int64_t n, int64_t* ou
 int rkv_schedule(const rkv_tree* t, int32_t Q, const int32_t* tok, const int64_t* tok_indptr,
                  int32_t* order, int64_t* matched);
 
+/* Radix keys for an image (or any non-text input) that occupies n_tokens
+ * positions of a request (the article's section "Resultados en modelos
+ * multimodales": the image's hash is the radix key, so requests with the
+ * same image reuse its tokens' KV).  *out_hash (nullable) = 64-bit FNV-1a of
+ * bytes[0..len); keys[i] = -1 - (splitmix64(hash + (i+1) * 0x9e3779b97f4a7c15)
+ * >> 33) for i < n_tokens (splitmix64 = its output finalizer), each in
+ * [-2^31, -1], so they never equal a text token id (>= 0).  Put them in the
+ * request's token sequence where the image's tokens sit; every tree call
+ * then treats them like tokens.  EINVAL on negative sizes or NULL buffers. */
+int rkv_image_keys(const uint8_t* bytes, int64_t len, int64_t n_tokens, int32_t* keys, uint64_t* out_hash);
+
 /* lock: +1 on the lock count of `node` and every ancestor up to, not
  * including, the root; locked nodes are never evicted.  unlock: -1 on the
  * same nodes; EINVAL (and no change) if any count would go negative or the

@@ -200,6 +200,40 @@ def c5e():
     return c5(1 << 19, "c5e")
 
 
+def mm_trace(seed: int = 9, images: int = 24, questions: int = 5, image_bytes: int = 4096,
+             system: int = 35, max_batch: int = 16):
+    """LLaVA-style visual question answering: every request is a shared
+    system prompt, one image and a question of U{8..48} fresh text tokens;
+    each image is asked `questions` questions.  Images are seeded random
+    bytes (their content, which the runtime hashes); requests come in a
+    seeded interleaved order, cut into batches of at most `max_batch` with no
+    image twice in a batch.  Returns (system tokens, image bytes list,
+    batches of (image index, question tokens))."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    sys_tokens = _fresh(rng, system)
+    blobs = [rng.integers(0, 256, size=image_bytes, dtype=np.uint8).tobytes() for _ in range(images)]
+    order = np.repeat(np.arange(images), questions)
+    rng.shuffle(order)
+    batches, cur, in_batch = [], [], set()
+    for img in order.tolist():
+        if len(cur) == max_batch or img in in_batch:
+            batches.append(cur)
+            cur, in_batch = [], set()
+        cur.append((img, _fresh(rng, int(rng.integers(8, 49)))))
+        in_batch.add(img)
+    if cur:
+        batches.append(cur)
+    return sys_tokens, blobs, batches
+
+
+def mm():
+    """LLaVA-v1.5-7B-shaped: 32 q / 32 kv heads, D=128, bf16; 576 image
+    positions per image (a 336-pixel image in 14-pixel patches); the
+    mm_trace requests.  Returns (shape, trace, image positions)."""
+    s = Shape("mm", 32, 32, 128, "bf16", 1 << 20, 9)
+    return s, mm_trace(s.seed), 576
+
+
 CONFIGS = {"c1": c1, "c2": c2, "c2s": c2s, "c3": c3, "c3ns": c3ns, "c4": c4, "c5": c5, "c5e": c5e}
 
 

@@ -31,7 +31,7 @@ EXPORTS = (
     "rkv_batch_commit", "rkv_kv_scatter", "rkv_attn_extend", "rkv_attn_decode_workspace_bytes",
     "rkv_attn_decode", "rkv_radix_peek", "rkv_schedule", "rkv_cascade_plan",
     "rkv_attn_decode_cascade_workspace_bytes", "rkv_attn_decode_cascade", "rkv_penalty_admit",
-    "rkv_penalty_accumulate", "rkv_penalty_apply",
+    "rkv_penalty_accumulate", "rkv_penalty_apply", "rkv_image_keys",
 )
 
 
@@ -89,6 +89,7 @@ def lib():
         "rkv_attn_decode_cascade": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32, _i32, _i32,
                                                    _i32, _i32, _f32, _i32, _vp, _vp, _vp, _vp, _i64, _i32,
                                                    _i32, _i32, _i64, _vp, _sz, _i64, _vp]),
+        "rkv_image_keys": (ctypes.c_int, [ctypes.c_char_p, _i64, _i64, c_i32p, ctypes.POINTER(ctypes.c_uint64)]),
         "rkv_penalty_admit": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
         "rkv_penalty_accumulate": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
         "rkv_penalty_apply": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp,
@@ -465,3 +466,13 @@ class PenaltyState:
             _ptr(freq), _ptr(pres), _ptr(rep), _ptr(min_new), _ptr(stop_indptr),
             _ptr(stop_ids) if stop_ids is not None and stop_ids.numel() else None, _ptr(new_tokens),
             _stream(stream)))
+
+
+def image_keys(data: bytes, n_tokens: int):
+    """Radix keys of an image occupying n_tokens positions: (int32 NumPy
+    array of n_tokens keys in [-2^31, -1], 64-bit content hash)."""
+    keys = np.empty(max(int(n_tokens), 1), dtype=np.int32)
+    h = ctypes.c_uint64()
+    _check(lib().rkv_image_keys(bytes(data), len(data), int(n_tokens), keys.ctypes.data_as(c_i32p),
+                                ctypes.byref(h)))
+    return keys[: int(n_tokens)], h.value

@@ -171,3 +171,17 @@ def test_decode_c4_sampled():
     ph = [phases[0], phases[1], phases[3]]
     res, _ = G.run(shape, ph, select=G.sample(4, 16), sparse=True)
     G.check(res, "bf16", "c4-decode")
+
+
+@pytest.mark.timeout(400)
+def test_extend_multimodal_hashed_images():
+    """LLaVA-shaped requests whose images enter the tree as content-hash keys
+    (rkv_image_keys): the first four batches, three sampled requests each;
+    later questions about an image extend only their question tokens."""
+    from prefix_shared_kv_host_amd import mm
+    s, trace, n_img = configs.mm()
+    seqs = mm.trace_batches(trace, n_img)[:4]
+    res, _ = G.run(s, [configs.Phase("extend", b) for b in seqs], select=G.sample(9, 3), sparse=True)
+    reused = [int(x) for r in res for x in r["batch"].host["prefix_lens"]]
+    assert max(reused) >= 35 + n_img              # an image's KV was reused
+    G.check(res, "bf16", "multimodal")
