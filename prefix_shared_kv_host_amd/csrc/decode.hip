@@ -78,6 +78,25 @@ struct SharedJobs {
   int32_t max_members;
 };
 
+// 16-byte K/V loads.  STREAM = non-temporal: measured on this chip, random
+// 256-byte to 4-KB row gathers reach ~6.7 TB/s with the hint and ~6.1 TB/s
+// without (a 4-GiB read: 7.0 vs 6.3 TB/s).  The hint pays only for rows that
+// no other request of the launch reads and that each instruction reads
+// whole: the private tails of a prefix-shared plan (c3 tails: 1227 -> 1128
+// us).  Plain decode keeps normal loads, because siblings there re-read
+// shared rows from L2/MALL (c3: 1288 -> 1417 us with the hint), and so do
+// the matrix-core K loads, which read half cache lines per instruction.
+typedef unsigned int kv_u32x4 __attribute__((ext_vector_type(4)));
+template <bool STREAM>
+__device__ __forceinline__ uint4 load_kv(const char* p) {
+  if constexpr (STREAM) {
+    const kv_u32x4 w = __builtin_nontemporal_load((const kv_u32x4*)p);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    return *(const uint4*)p;
+  }
+}
+
 __host__ __device__ inline int split_chunk(int L, int num_splits) {
   if (num_splits <= 0) return kChunk;
   int c = (L + num_splits - 1) / num_splits;
@@ -244,7 +263,7 @@ __device__ __forceinline__ void walk(const DecodeArgs& a, const int32_t* row_tab
       const int32_t sl = __shfl(slots, key_of(kb, l16));
       const char* rowp = kg + (uint64_t)(uint32_t)sl * slot_bytes;
 #pragma unroll
-      for (int k = 0; k < KSTEPS; ++k) kreg[kb][k] = *(const uint4*)(rowp + k * 64);
+      for (int k = 0; k < KSTEPS; ++k) kreg[kb][k] = load_kv<false>(rowp + k * 64);
     }
   };
   auto dma_v = [&](int32_t slots, int stage) {
@@ -586,8 +605,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CB > 0 ? 2 
         slot = 0;
       }
       const uint64_t off = (uint64_t)(uint32_t)slot * slot_bytes;
-      kr[u] = *(const uint4*)(kbase + off);
-      vr[u] = *(const uint4*)(vbase + off);
+      kr[u] = load_kv<(CB > 0)>(kbase + off);
+      vr[u] = load_kv<(CB > 0)>(vbase + off);
     }
     if (base + step < k_end) fetch_slots(base + step);
     float sc[U][G];
