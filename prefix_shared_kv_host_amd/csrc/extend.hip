@@ -13,14 +13,16 @@
 //     heads share every K/V tile they read.  Work items are ordered kv-head
 //     major and dealt to XCDs in contiguous ranges (requests sharing a prefix
 //     read the same rows of one head from one L2).
-//   * 4 waves x 32 rows.  Each wave keeps its Q (two 16-row blocks) in
-//     registers for the whole key loop.
-//   * K/V tiles of 64 keys are gathered row by row (16-byte loads, one slot
-//     lookup per row) into registers one tile ahead, then written to LDS: K
-//     as rows, V transposed (d-major) so both MFMA operands are single 16-byte
-//     LDS reads.
+//   * 4 waves x 32 rows, two workgroups per CU.  Each wave keeps its Q (two
+//     16-row blocks) in registers for the whole key loop.
+//   * K/V tiles of 64 keys go global -> LDS by 16-byte LDS DMA
+//     (global_load_lds), one slot lookup per row: K two tiles ahead, V one,
+//     each in two stages; the slot indices reach LDS by 4-byte DMA straight
+//     from the table.  The gathers of a tile are spread over the next tile's
+//     QK steps.  K is read as 16-byte rows (ds_read_b128); V stays row-major
+//     and the V^T operand comes from transposed reads (ds_read_b64_tr_b16).
 //   * S^T = K Q^T, so a lane owns one query: its row max / row sum are lane
-//     values plus a 4-lane exchange.  K rows are placed in LDS in an order
+//     values plus cross-lane swaps.  K rows are placed in LDS in an order
 //     that makes the S^T accumulator of a lane hold 8 consecutive keys, which
 //     is exactly the bf16 B operand of O^T += V^T P^T: the softmax weights
 //     never leave registers.

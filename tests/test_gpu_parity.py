@@ -157,20 +157,39 @@ def test_decode_tiny_ragged(dtype, hq, hkv, d, splits):
     G.check(res, dtype, f"decode {dtype} {hq}/{hkv} d{d} s{splits}")
 
 
+def _decode_only(i, B):
+    """Checks every request of the decode phase, none of the setup phases."""
+    return None
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("cascade", [None, {}], ids=["plain", "prefix-shared"])
+def test_decode_c3_every_request(cascade):
+    """All 256 requests x 32 heads of the radix-tree decode batch, through
+    plain decode and through the prefix-shared path the bench times."""
+    shape, phases = configs.build("c3")
+    res, _ = G.run(shape, phases, select=_decode_only, cascade=cascade)
+    assert [len(r["requests"]) for r in res] == [256]
+    G.check(res, "bf16", "c3 " + ("plain" if cascade is None else "prefix-shared"))
+
+
 @pytest.mark.timeout(400)
-@pytest.mark.parametrize("name", ["c3", "c3ns"])
-def test_decode_c3_sampled(name):
-    shape, phases = configs.build(name)
+def test_decode_c3ns_sampled():
+    shape, phases = configs.build("c3ns")
     res, _ = G.run(shape, phases, select=G.sample(3, 24), sparse=True)
-    G.check(res, "bf16", name)
+    G.check(res, "bf16", "c3ns")
 
 
-@pytest.mark.timeout(400)
-def test_decode_c4_sampled():
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("cascade", [None, {}], ids=["plain", "prefix-shared"])
+def test_decode_c4_every_request(cascade):
+    """All 64 decode requests x 64 heads of the grouped-head workload (one
+    2048-token prefix), plain and prefix-shared."""
     shape, phases = configs.c4()
     ph = [phases[0], phases[1], phases[3]]
-    res, _ = G.run(shape, ph, select=G.sample(4, 16), sparse=True)
-    G.check(res, "bf16", "c4-decode")
+    res, _ = G.run(shape, ph, select=_decode_only, cascade=cascade)
+    assert [len(r["requests"]) for r in res] == [64]
+    G.check(res, "bf16", "c4-decode " + ("plain" if cascade is None else "prefix-shared"))
 
 
 @pytest.mark.timeout(400)
