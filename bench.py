@@ -157,17 +157,19 @@ class Phase:
         self.cache.decode(self.batch, self.q, self.o, self.lse)
 
 
-def gqa_halves(steps, warmup):
+def gqa_halves(steps, warmup, cfg=None):
     """Llama-70B-shaped GQA (c4: 64 q / 8 kv heads, D=128, bf16, a shared
     2048-token prefix): the extend half (64 requests x 256 new tokens) and the
     decode half (64 requests x 1 token), each kv_scatter + attention, timed
-    with HIP events on the launch stream; reported separately and summed."""
+    with HIP events on the launch stream; reported separately and summed.
+    cfg: another config with c4's phases (its heads may differ)."""
     import torch
     from inputs import configs
+    cfg = configs.c4 if cfg is None else cfg
     stream = torch.cuda.current_stream()
     out = {}
     for name, idx in (("extend", 2), ("decode", 3)):
-        ph = Phase("c4-" + name, configs.c4, idx)
+        ph = Phase("c4-" + name, cfg, idx)
         for _ in range(warmup):
             ph.scatter()
             ph.attend()
@@ -212,6 +214,22 @@ def gqa_halves(steps, warmup):
     out["workload"] = ("llama70b-gqa: 128 requests share a 2048-token prefix; 64 extend 256 tokens (contexts "
                        "2304-8192), 64 decode 1 token (contexts 2049-8192); 64/8 heads, D=128, bf16, 2^20 slots")
     return out
+
+
+def tp8_share(steps, warmup):
+    """One GPU's share of 8-way tensor parallelism over heads, at real shape:
+    c4 with 8 q / 1 kv heads per GPU (both halves), c5 with 4 q / 1 kv heads
+    (the chat replay).  The all-reduce after the attention projection is
+    outside this path and not modelled."""
+    from inputs import configs
+    c4s = gqa_halves(steps, warmup, configs.c4tp8)
+    c4s["workload"] = ("llama70b-gqa, one GPU of 8-way tensor parallelism: 8 q / 1 kv heads, the c4 requests "
+                       "(64 extend 256 tokens, 64 decode 1 token, 2048-token shared prefix)")
+    s, phases = configs.c5tp8()
+    replay(s, phases[:4])
+    c5s = replay(s, phases)
+    c5s["workload"] = "c5 chat replay, one GPU of 8-way tensor parallelism: 4 q / 1 kv heads, 2^21 slots"
+    return {"c4tp8": c4s, "c5tp8": c5s}
 
 
 def chat_pipeline(name):
@@ -673,6 +691,7 @@ def main():
     del ext, dec
     torch.cuda.empty_cache()
     out["gqa_llama70b"] = gqa_halves(max(5, args.steps // 2), 3)
+    out["tp8_share"] = tp8_share(max(5, args.steps // 2), 3)
     out["chat_pipeline"] = [chat_pipeline("c5"), chat_pipeline("c5e")]
     out["cache_aware_scheduling"] = queue_orders()
     out["sampling_penalties"] = sampling_penalties()

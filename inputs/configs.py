@@ -200,6 +200,20 @@ def c5e():
     return c5(1 << 19, "c5e")
 
 
+def c4tp8():
+    """One GPU's share of c4 under 8-way tensor parallelism over heads: the
+    same requests, with this GPU's 8 q heads and 1 kv head."""
+    s, phases = c4()
+    return Shape("c4tp8", 8, 1, s.d, s.dtype, s.pool, s.seed), phases
+
+
+def c5tp8():
+    """One GPU's share of c5 under 8-way tensor parallelism: 4 q heads and 1
+    kv head per GPU, the same chat trace."""
+    s, phases = c5()
+    return Shape("c5tp8", 4, 1, s.d, s.dtype, s.pool, s.seed), phases
+
+
 def mm_trace(seed: int = 9, images: int = 24, questions: int = 5, image_bytes: int = 4096,
              system: int = 35, max_batch: int = 16):
     """LLaVA-style visual question answering: every request is a shared
@@ -234,7 +248,8 @@ def mm():
     return s, mm_trace(s.seed), 576
 
 
-CONFIGS = {"c1": c1, "c2": c2, "c2s": c2s, "c3": c3, "c3ns": c3ns, "c4": c4, "c5": c5, "c5e": c5e}
+CONFIGS = {"c1": c1, "c2": c2, "c2s": c2s, "c3": c3, "c3ns": c3ns, "c4": c4, "c5": c5, "c5e": c5e,
+           "c4tp8": c4tp8, "c5tp8": c5tp8}
 
 
 def build(name: str):

@@ -204,3 +204,31 @@ def test_extend_multimodal_hashed_images():
     reused = [int(x) for r in res for x in r["batch"].host["prefix_lens"]]
     assert max(reused) >= 35 + n_img              # an image's KV was reused
     G.check(res, "bf16", "multimodal")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("cascade", [None, {}], ids=["plain", "prefix-shared"])
+def test_decode_c4tp8_every_request(cascade):
+    """One GPU's share of c4 under 8-way tensor parallelism (8 q heads, 1 kv
+    head): every decode request."""
+    shape, phases = configs.c4tp8()
+    res, _ = G.run(shape, [phases[0], phases[1], phases[3]], select=_decode_only, cascade=cascade)
+    assert [len(r["requests"]) for r in res] == [64]
+    G.check(res, "bf16", "c4tp8-decode " + ("plain" if cascade is None else "prefix-shared"))
+
+
+@pytest.mark.timeout(600)
+def test_extend_c4tp8_subset():
+    """The extend half of one GPU's c4 share: 8 sampled requests, all rows."""
+    shape, phases = configs.c4tp8()
+    res, _ = G.run(shape, phases[:3], select=G.sample(8, 8), sparse=True)
+    G.check(res, "bf16", "c4tp8-extend")
+
+
+@pytest.mark.timeout(600)
+def test_extend_c5tp8_batches():
+    """One GPU's share of the chat trace (4 q heads, 1 kv head): the first
+    four batches, three sampled turns each."""
+    shape, phases = configs.c5tp8()
+    res, _ = G.run(shape, phases[:4], select=G.sample(10, 3), sparse=True)
+    G.check(res, "bf16", "c5tp8")
