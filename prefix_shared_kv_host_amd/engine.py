@@ -23,7 +23,7 @@ POISON = {torch.bfloat16: 0x7FC0, torch.float32: 0x7FC00000}
 
 @dataclass
 class Batch:
-    seqs: list
+    seqs: object                # the token ids as given (lists or an rkv.TokenBatch)
     host: dict                  # NumPy tables from batch_prepare
     req_to_token: torch.Tensor  # device int32 [B, ld]
     qo_indptr: torch.Tensor
@@ -55,6 +55,10 @@ class RadixKVCache:
 
     # ---------------------------------------------------------------- host
     def prepare(self, seqs, ld=None) -> Batch:
+        """seqs: a list of token-id sequences or an rkv.TokenBatch (converted
+        once here either way and reused by commit)."""
+        if not isinstance(seqs, rkv.TokenBatch):
+            seqs = rkv.TokenBatch(seqs)
         code, tb = self.tree.batch_prepare(seqs, ld)
         if code != rkv.OK:
             raise rkv.RkvError(code, "batch_prepare: eviction cannot free enough slots")

@@ -10,6 +10,7 @@ message.
 from __future__ import annotations
 
 import ctypes
+import itertools
 import math
 import os
 
@@ -33,6 +34,23 @@ EXPORTS = (
     "rkv_attn_decode_cascade_workspace_bytes", "rkv_attn_decode_cascade", "rkv_penalty_admit",
     "rkv_penalty_accumulate", "rkv_penalty_apply", "rkv_image_keys",
 )
+
+
+class TokenBatch:
+    """Token ids of a batch as one int32 array with int64 offsets (request r
+    is flat[indptr[r]:indptr[r+1]]); the tree calls take it in place of a
+    list of sequences, so a batch is converted once for prepare and commit."""
+
+    def __init__(self, seqs):
+        self.lens = np.array([len(x) for x in seqs], dtype=np.int64)
+        self.indptr = np.zeros(len(self.lens) + 1, dtype=np.int64)
+        np.cumsum(self.lens, out=self.indptr[1:])
+        total = int(self.indptr[-1])
+        self.flat = np.fromiter(itertools.chain.from_iterable(seqs), dtype=np.int32, count=total) \
+            if total else np.zeros(0, dtype=np.int32)
+
+    def __len__(self):
+        return len(self.lens)
 
 
 class RkvError(RuntimeError):
@@ -230,6 +248,8 @@ class Tree:
     # -- batches ------------------------------------------------------------
     @staticmethod
     def _flat(seqs):
+        if isinstance(seqs, TokenBatch):
+            return seqs.flat, seqs.indptr, seqs.lens
         lens = np.array([len(s) for s in seqs], dtype=np.int64)
         indptr = np.zeros(len(seqs) + 1, dtype=np.int64)
         np.cumsum(lens, out=indptr[1:])

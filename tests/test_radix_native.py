@@ -56,3 +56,26 @@ def test_chat_trace_tables_bit_exact(name):
         assert s[7] > 100000      # the 2^19 pool really evicts
     else:
         assert s[7] == 0          # the 2^21 pool never binds
+
+
+def test_token_batch_equals_lists():
+    """Token ids given as an rkv.TokenBatch (one int32 array and offsets)
+    produce the same tables, tree and free list as the same ids as lists."""
+    import numpy as np
+    from inputs import configs
+    from prefix_shared_kv_host_amd import rkv
+    s, phases = configs.build("c2")
+    a = rkv.Tree(4096 * 64, None)
+    b = rkv.Tree(4096 * 64, None)
+    for ph in phases:
+        seqs = [x[:200] for x in ph.seqs[:16]]
+        tk = rkv.TokenBatch(seqs)
+        assert len(tk) == len(seqs) and tk.flat.dtype == np.int32
+        ca, ta = a.batch_prepare(seqs)
+        cb, tbb = b.batch_prepare(tk)
+        assert ca == cb == rkv.OK
+        for key in ("req_to_token", "prefix_lens", "seq_lens", "qo_indptr", "new_slots"):
+            assert np.array_equal(ta[key], tbb[key]), key
+        a.batch_commit(seqs, ta["req_to_token"], ta["nodes"])
+        b.batch_commit(tk, tbb["req_to_token"], tbb["nodes"])
+        assert a.radix_serialize() == b.radix_serialize()
