@@ -229,8 +229,8 @@ struct State {
 // range and into the pool.
 template <int D, int CB>
 __device__ __forceinline__ void walk(const DecodeArgs& a, const int32_t* row_tab, int k_begin, int k_end, int g,
-                                     const bf16x8 (&q)[CB][D / 32], int ncb, State<D, CB>& st,
-                                     char (&Vs)[2][32 * D * 2]) {
+                                     const bf16x8 (&q)[CB][D / 32], int ncb, State<D, CB>& st, char* V0,
+                                     char* V1) {
   constexpr int ROWB = D * 2;
   constexpr int CH = D / 8;
   constexpr int KSTEPS = D / 32;
@@ -247,15 +247,19 @@ __device__ __forceinline__ void walk(const DecodeArgs& a, const int32_t* row_tab
   const uint32_t slot_bytes = (uint32_t)a.hkv * ROWB;
   const char* kg = (const char*)a.kp + (uint64_t)g * ROWB + gq * 16;
   const char* vg = (const char*)a.vp + (uint64_t)g * ROWB;
-  // lane (lane & 31) holds the slot of key base + (lane & 31)
-  auto fetch = [&](int base) -> int32_t {
-    int32_t slot = row_tab[min(base + (lane & 31), k_end - 1)];
+  // lane (lane & 31) loads the slot of key base + (lane & 31).  Its range
+  // check (checked) is taken where the slots are used, one step later: a
+  // test right after the load would wait for every gather still in flight.
+  auto fetch = [&](int base) -> int32_t { return row_tab[min(base + (lane & 31), k_end - 1)]; };
+  auto checked = [&](int32_t slot) -> int32_t {
     if ((uint32_t)slot >= P) {
       if (a.err) rkv::raise_flag(a.err);
       slot = 0;
     }
     return slot;
   };
+  // K operands of one step; refilled for the next step as soon as the
+  // score products have read them
   uint4 kreg[2][KSTEPS];
   auto load_k = [&](int32_t slots) {
 #pragma unroll
@@ -266,7 +270,7 @@ __device__ __forceinline__ void walk(const DecodeArgs& a, const int32_t* row_tab
       for (int k = 0; k < KSTEPS; ++k) kreg[kb][k] = load_kv<false>(rowp + k * 64);
     }
   };
-  auto dma_v = [&](int32_t slots, int stage) {
+  auto dma_v = [&](int32_t slots, char* dst) {
     const int drow = lane / CH, dch = lane % CH;
 #pragma unroll
     for (int j = 0; j < NDMA; ++j) {
@@ -274,48 +278,68 @@ __device__ __forceinline__ void walk(const DecodeArgs& a, const int32_t* row_tab
       const int32_t sl = __shfl(slots, R);
       const int lch = dch ^ swz_v<CH>(R);
       __builtin_amdgcn_global_load_lds((const void*)(vg + (uint64_t)(uint32_t)sl * slot_bytes + lch * 16),
-                                       (RKV_LDS void*)(Vs[stage] + j * 1024), 16, 0, 0);
+                                       (RKV_LDS void*)(dst + j * 1024), 16, 0, 0);
     }
   };
-
-  int32_t slots = fetch(k_begin);
-  load_k(slots);
-  dma_v(slots, 0);
-  int stage = 0;
-  for (int base = k_begin; base < k_end; base += STEP) {
-    __builtin_amdgcn_s_waitcnt(0);          // K operands and this step's V tile are in
-    bf16x8 ka[2][KSTEPS];
+  // K(k_begin) in registers and V(k_begin) in stage V0; the slots of each
+  // next step are fetched a step ahead
+  {
+    const int32_t s0 = checked(fetch(k_begin));
+    load_k(s0);
+    dma_v(s0, V0);
+  }
+  int32_t nslot = 0;
+  if (k_begin + STEP < k_end) nslot = fetch(k_begin + STEP);
+  // One 32-key step on the K operands in kreg and the V tile in `cur`; with
+  // LOAD it issues the next step's gathers (K into kreg once the score
+  // products have read it, V into `nxt`).  The stages are fixed at compile
+  // time, and the loads happen unconditionally inside a step, so that
+  // nothing waits for a gather it does not read:
+  //   - with a run-time LDS stage index the compiler cannot tell the
+  //     transposed reads from the DMA still in flight and waits for all of it
+  //     before them;
+  //   - a conditional load into registers becomes a copy at the join, which
+  //     waits for the load.
+  // Either puts one full memory latency into every step.
+  auto step = [&](int base, char* cur, char* nxt, auto load_tag) {
+    constexpr bool LOAD = decltype(load_tag)::value;
+    // the scheduler may not pull this step's products above the wait (it
+    // would then wait in the previous step for these gathers)
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0);          // K operands, this step's V tile and the next slots are in
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 sacc[CB][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int cb = 0; cb < CB; ++cb) {
+      if (cb >= ncb) break;
 #pragma unroll
-      for (int k = 0; k < KSTEPS; ++k) ka[kb][k] = __builtin_bit_cast(bf16x8, kreg[kb][k]);
-    const bool more = base + STEP < k_end;
-    if (more) {
-      slots = fetch(base + STEP);
-      load_k(slots);
-      dma_v(slots, stage ^ 1);
+      for (int kb = 0; kb < 2; ++kb) {
+        sacc[cb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < KSTEPS; ++k)
+          sacc[cb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[kb][k]), q[cb][k],
+                                                                 sacc[cb][kb], 0, 0, 0);
+      }
+    }
+    if constexpr (LOAD) {
+      nslot = checked(nslot);
+      load_k(nslot);
+      dma_v(nslot, nxt);
+      if (base + 2 * STEP < k_end) nslot = fetch(base + 2 * STEP);
     }
     // lane (column l16, group gq) holds keys base + 8*gq + 4*kb + i
-    const int lim = k_end - 1 - base - 8 * gq;
+    const int lim = k_end - 1 - base;
     bf16x8 pb[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       if (cb >= ncb) break;
-      f32x4 sacc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int k = 0; k < KSTEPS; ++k)
-          sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb][k], q[cb][k], sacc[kb], 0, 0, 0);
-      }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (4 * kb + i > lim) sacc[kb][i] = -INFINITY;
-      float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
-                       fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
+          if (8 * gq + 4 * kb + i > lim) sacc[cb][kb][i] = -INFINITY;
+      float mx = fmaxf(fmaxf(fmaxf(sacc[cb][0][0], sacc[cb][0][1]), fmaxf(sacc[cb][0][2], sacc[cb][0][3])),
+                       fmaxf(fmaxf(sacc[cb][1][0], sacc[cb][1][1]), fmaxf(sacc[cb][1][2], sacc[cb][1][3])));
       mx = rkv::max_xor16(mx);
       mx = rkv::max_xor32(mx);
       const float mt = mx * c;
@@ -331,14 +355,14 @@ __device__ __forceinline__ void walk(const DecodeArgs& a, const int32_t* row_tab
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int kb = e >> 1, i = 2 * (e & 1);
-        wv[e] = rkv::pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c, -st.m[cb])),
-                                 __builtin_amdgcn_exp2f(fmaf(sacc[kb][i + 1], c, -st.m[cb])));
+        wv[e] = rkv::pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sacc[cb][kb][i], c, -st.m[cb])),
+                                 __builtin_amdgcn_exp2f(fmaf(sacc[cb][kb][i + 1], c, -st.m[cb])));
       }
       pb[cb] = __builtin_bit_cast(bf16x8, make_uint4(wv[0], wv[1], wv[2], wv[3]));
       st.l[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[cb], st.l[cb], 0, 0, 0);
     }
     // PV: one V^T operand of this tile at a time, reused by every block
-    const char* vs = Vs[stage];
+    const char* vs = cur;
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) {
       v4i16 part[2];
@@ -358,7 +382,19 @@ __device__ __forceinline__ void walk(const DecodeArgs& a, const int32_t* row_tab
         st.o[cb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[cb], st.o[cb][db], 0, 0, 0);
       }
     }
-    stage ^= 1;
+  };
+  using Load = std::true_type;
+  using Last = std::false_type;
+  int base = k_begin;
+  for (; base + 2 * STEP < k_end; base += 2 * STEP) {   // both steps have a successor
+    step(base, V0, V1, Load{});
+    step(base + STEP, V1, V0, Load{});
+  }
+  if (base + STEP < k_end) {
+    step(base, V0, V1, Load{});
+    step(base + STEP, V1, V0, Last{});
+  } else {
+    step(base, V0, V1, Last{});
   }
   __builtin_amdgcn_s_waitcnt(0);
 }
@@ -389,7 +425,7 @@ __device__ __forceinline__ void store_partial(float* dst, const f32x4 (&o)[D / 1
 }  // namespace gqa
 
 template <int D>
-__device__ __forceinline__ void gqa_item(const DecodeArgs& a, int64_t w, char (&Vs)[2][32 * D * 2]) {
+__device__ __forceinline__ void gqa_item(const DecodeArgs& a, int64_t w, char* V0, char* V1) {
   using namespace gqa;
   const int s = (int)(w % a.splits);
   int64_t rest = w / a.splits;
@@ -411,7 +447,7 @@ __device__ __forceinline__ void gqa_item(const DecodeArgs& a, int64_t w, char (&
   for (int db = 0; db < D / 16; ++db) st.o[0][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   st.l[0] = f32x4{0.f, 0.f, 0.f, 0.f};
   st.m[0] = -INFINITY;
-  walk<D, 1>(a, a.r2t + (int64_t)r * a.ld, k_begin, k_end, g, qreg, 1, st, Vs);
+  walk<D, 1>(a, a.r2t + (int64_t)r * a.ld, k_begin, k_end, g, qreg, 1, st, V0, V1);
   if (!hvalid) return;
   const float lsum = st.l[0][0];
   if (rec < 0) {
@@ -433,8 +469,8 @@ __device__ __forceinline__ void gqa_item(const DecodeArgs& a, int64_t w, char (&
 // q head g*G + c % G.  The plan's values are checked against the batch
 // before use; a job that does not fit is skipped (flag raised in debug mode).
 template <int D, int CB>
-__device__ __forceinline__ void shared_item(const DecodeArgs& a, const SharedJobs& j, int64_t w,
-                                            char (&Vs)[2][32 * D * 2]) {
+__device__ __forceinline__ void shared_item(const DecodeArgs& a, const SharedJobs& j, int64_t w, char* V0,
+                                            char* V1) {
   using namespace gqa;
   const int job = (int)(w % j.n_jobs);
   const int g = (int)(w / j.n_jobs);
@@ -478,7 +514,7 @@ __device__ __forceinline__ void shared_item(const DecodeArgs& a, const SharedJob
     st.l[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
     st.m[cb] = -INFINITY;
   }
-  walk<D, CB>(a, a.r2t + (int64_t)rep * a.ld, kb, ke, g, qreg, ncb, st, Vs);
+  walk<D, CB>(a, a.r2t + (int64_t)rep * a.ld, kb, ke, g, qreg, ncb, st, V0, V1);
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     if (!valid[cb]) continue;
@@ -517,12 +553,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CB > 0 ? 2 
   extern __shared__ float red[];
   int64_t w;
   if constexpr (CB > 0) {
-    __shared__ __attribute__((aligned(16))) char Vs[4][2][32 * D * 2];
+    // the two V stages of each wave, as two arrays (see walk)
+    __shared__ __attribute__((aligned(16))) char V0[4][32 * D * 2];
+    __shared__ __attribute__((aligned(16))) char V1[4][32 * D * 2];
     const int b = (int)blockIdx.x;
     if (b < shared_blocks) {
       const int wave = (int)(threadIdx.x >> 6);
       const int64_t item = rkv::xcd_work_item(b, shared_blocks) * 4 + wave;
-      if (item < (int64_t)j.n_jobs * a.hkv) shared_item<D, CB>(a, j, item, Vs[wave]);
+      if (item < (int64_t)j.n_jobs * a.hkv) shared_item<D, CB>(a, j, item, V0[wave], V1[wave]);
       return;
     }
     w = rkv::xcd_work_item(b - shared_blocks, (int64_t)gridDim.x - shared_blocks);
@@ -699,10 +737,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CB > 0 ? 2 
   }
 }
 
+// Two waves per SIMD: without the hint the two-stage walk takes more than
+// 256 registers at D = 128 and runs one.
 template <int D>
-__global__ __launch_bounds__(64) void decode_gqa(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) char Vs[2][32 * D * 2];
-  gqa_item<D>(a, rkv::xcd_work_item(blockIdx.x, gridDim.x), Vs);
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_gqa(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) char V0[32 * D * 2];
+  __shared__ __attribute__((aligned(16))) char V1[32 * D * 2];
+  gqa_item<D>(a, rkv::xcd_work_item(blockIdx.x, gridDim.x), V0, V1);
 }
 
 // Prefix-shared phase 1 in one launch when the tails run on the matrix
@@ -715,14 +756,15 @@ __global__ __launch_bounds__(64) void decode_gqa(DecodeArgs a) {
 template <int D, int CB>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_cascade_mfma(
     DecodeArgs a, SharedJobs j, int32_t shared_blocks) {
-  __shared__ __attribute__((aligned(16))) char Vs[2][32 * D * 2];
+  __shared__ __attribute__((aligned(16))) char V0[32 * D * 2];
+  __shared__ __attribute__((aligned(16))) char V1[32 * D * 2];
   const int b = (int)blockIdx.x;
   if (b < shared_blocks) {
     const int64_t w = rkv::xcd_work_item(b, shared_blocks);
-    if (w < (int64_t)j.n_jobs * a.hkv) shared_item<D, CB>(a, j, w, Vs);
+    if (w < (int64_t)j.n_jobs * a.hkv) shared_item<D, CB>(a, j, w, V0, V1);
     return;
   }
-  gqa_item<D>(a, rkv::xcd_work_item(b - shared_blocks, (int64_t)gridDim.x - shared_blocks), Vs);
+  gqa_item<D>(a, rkv::xcd_work_item(b - shared_blocks, (int64_t)gridDim.x - shared_blocks), V0, V1);
 }
 
 // Phase 2: one wave per (request, q head); lanes cover D.
