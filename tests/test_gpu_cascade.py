@@ -67,6 +67,9 @@ CASES = [
     (12, 2, 128, dict(seg_chunk=160, tail_chunk=768, min_keys=4)),
     (3, 1, 128, dict(seg_chunk=256, tail_chunk=384, min_keys=32, max_members=3)),
     (2, 2, 64, dict(seg_chunk=32, tail_chunk=64, min_keys=1)),
+    # chunks of 33 and 65 keys: every shared and tail item ends inside a
+    # 32-key step of the grouped-head walk
+    (16, 2, 128, dict(seg_chunk=33, tail_chunk=65, min_keys=1)),
 ]
 
 

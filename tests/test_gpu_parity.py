@@ -157,6 +157,20 @@ def test_decode_tiny_ragged(dtype, hq, hkv, d, splits):
     G.check(res, dtype, f"decode {dtype} {hq}/{hkv} d{d} s{splits}")
 
 
+@pytest.mark.parametrize("hq,hkv,d,splits", [(16, 2, 128, 0), (16, 2, 128, 3), (32, 8, 64, 0), (32, 8, 64, 5)])
+def test_decode_matrix_core_every_length(hq, hkv, d, splits):
+    """The grouped-head walk (>= 4 query heads per kv head, bf16) steps
+    through a split 32 keys at a time, two steps per loop trip, with the last
+    one or two steps outside the loop: every length 1..96 (every residue of
+    32 and 64, one to three trips), whole or cut into 3 or 5 splits that
+    start at arbitrary keys."""
+    shape = configs.Shape(f"dec-mc-{hq}-{hkv}-{d}-{splits}", hq, hkv, d, "bf16", 16384, 61)
+    lens = list(range(1, 97))
+    phases = decode_workload(shape, lens, shared=40, seed=hq + d + splits)
+    res, _ = G.run(shape, phases, num_splits=splits, content_device="cpu")
+    G.check(res, "bf16", f"decode every length {hq}/{hkv} d{d} s{splits}")
+
+
 def _decode_only(i, B):
     """Checks every request of the decode phase, none of the setup phases."""
     return None
