@@ -85,8 +85,14 @@ struct SharedJobs {
 // whole: the private tails of a prefix-shared plan (c3 tails: 1227 -> 1128
 // us).  Plain decode keeps normal loads, because siblings there re-read
 // shared rows from L2/MALL (c3: 1288 -> 1417 us with the hint), and so do
-// the matrix-core K loads, which read half cache lines per instruction.
+// the matrix-core K loads, which read half cache lines per instruction.  The
+// matrix-core V tiles (whole rows per DMA instruction) stream for the tails
+// of large prefix-shared launches.  For the shared runs the hint gains 2 %
+// on back-to-back decode launches but loses 1-3 % when the decode follows an
+// extend step (c3), so they keep normal loads.
 typedef unsigned int kv_u32x4 __attribute__((ext_vector_type(4)));
+// cache-policy operand of an LDS-DMA load that marks it non-temporal
+constexpr int kNonTemporal = 2;
 template <bool STREAM>
 __device__ __forceinline__ uint4 load_kv(const char* p) {
   if constexpr (STREAM) {
@@ -226,8 +232,8 @@ struct State {
 // Walks keys [k_begin, k_end) of row_tab for kv head g; q[cb][k] is the Q^T
 // operand of block cb (columns l16, rows d = k*32 + 8*gq + [0..7]).  Blocks
 // cb >= ncb (wave-uniform) are skipped.  Every gather is clamped into the
-// range and into the pool.
-template <int D, int CB>
+// range and into the pool.  VSTREAM: the V tiles are fetched non-temporally.
+template <int D, int CB, bool VSTREAM>
 __device__ __forceinline__ void walk(const DecodeArgs& a, const int32_t* row_tab, int k_begin, int k_end, int g,
                                      const bf16x8 (&q)[CB][D / 32], int ncb, State<D, CB>& st, char* V0,
                                      char* V1) {
@@ -278,7 +284,7 @@ __device__ __forceinline__ void walk(const DecodeArgs& a, const int32_t* row_tab
       const int32_t sl = __shfl(slots, R);
       const int lch = dch ^ swz_v<CH>(R);
       __builtin_amdgcn_global_load_lds((const void*)(vg + (uint64_t)(uint32_t)sl * slot_bytes + lch * 16),
-                                       (RKV_LDS void*)(dst + j * 1024), 16, 0, 0);
+                                       (RKV_LDS void*)(dst + j * 1024), 16, 0, VSTREAM ? kNonTemporal : 0);
     }
   };
   // K(k_begin) in registers and V(k_begin) in stage V0; the slots of each
@@ -424,7 +430,7 @@ __device__ __forceinline__ void store_partial(float* dst, const f32x4 (&o)[D / 1
 }
 }  // namespace gqa
 
-template <int D>
+template <int D, bool VSTREAM>
 __device__ __forceinline__ void gqa_item(const DecodeArgs& a, int64_t w, char* V0, char* V1) {
   using namespace gqa;
   const int s = (int)(w % a.splits);
@@ -447,7 +453,7 @@ __device__ __forceinline__ void gqa_item(const DecodeArgs& a, int64_t w, char* V
   for (int db = 0; db < D / 16; ++db) st.o[0][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   st.l[0] = f32x4{0.f, 0.f, 0.f, 0.f};
   st.m[0] = -INFINITY;
-  walk<D, 1>(a, a.r2t + (int64_t)r * a.ld, k_begin, k_end, g, qreg, 1, st, V0, V1);
+  walk<D, 1, VSTREAM>(a, a.r2t + (int64_t)r * a.ld, k_begin, k_end, g, qreg, 1, st, V0, V1);
   if (!hvalid) return;
   const float lsum = st.l[0][0];
   if (rec < 0) {
@@ -514,7 +520,7 @@ __device__ __forceinline__ void shared_item(const DecodeArgs& a, const SharedJob
     st.l[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
     st.m[cb] = -INFINITY;
   }
-  walk<D, CB>(a, a.r2t + (int64_t)rep * a.ld, kb, ke, g, qreg, ncb, st, V0, V1);
+  walk<D, CB, false>(a, a.r2t + (int64_t)rep * a.ld, kb, ke, g, qreg, ncb, st, V0, V1);
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     if (!valid[cb]) continue;
@@ -743,7 +749,7 @@ template <int D>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_gqa(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char V0[32 * D * 2];
   __shared__ __attribute__((aligned(16))) char V1[32 * D * 2];
-  gqa_item<D>(a, rkv::xcd_work_item(blockIdx.x, gridDim.x), V0, V1);
+  gqa_item<D, false>(a, rkv::xcd_work_item(blockIdx.x, gridDim.x), V0, V1);
 }
 
 // Prefix-shared phase 1 in one launch when the tails run on the matrix
@@ -753,7 +759,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 // latency-bound, before them.  Each range has its own XCD-aware order.  Two
 // waves per SIMD: the register budget of 256 per lane holds CB = 2 at
 // D = 128 (without the hint the compiler takes more and runs one).
-template <int D, int CB>
+// TAIL_STREAM: the tails' V tiles come in by non-temporal DMA (their rows are
+// read by no other item); chosen by the host for launches with many tail
+// items (see launch_cascade_cb).
+template <int D, int CB, bool TAIL_STREAM>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_cascade_mfma(
     DecodeArgs a, SharedJobs j, int32_t shared_blocks) {
   __shared__ __attribute__((aligned(16))) char V0[32 * D * 2];
@@ -764,7 +773,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     if (w < (int64_t)j.n_jobs * a.hkv) shared_item<D, CB>(a, j, w, V0, V1);
     return;
   }
-  gqa_item<D>(a, rkv::xcd_work_item(b - shared_blocks, (int64_t)gridDim.x - shared_blocks), V0, V1);
+  gqa_item<D, TAIL_STREAM>(a, rkv::xcd_work_item(b - shared_blocks, (int64_t)gridDim.x - shared_blocks), V0, V1);
 }
 
 // Phase 2: one wave per (request, q head); lanes cover D.
@@ -849,6 +858,7 @@ void launch_all(const DecodeArgs& a, int64_t grid, hipStream_t st) {
 // Query columns per prefix-shared wave: two 16-column blocks at D = 128 and
 // four at D = 64 fit two waves per SIMD without spills.
 constexpr int kMaxSharedColumns(int d) { return d == 128 ? 32 : 64; }
+constexpr int64_t kStreamTailItems = 2048;
 
 template <int D, int CB>
 void launch_cascade_cb(const DecodeArgs& a, const SharedJobs& j, hipStream_t st) {
@@ -858,8 +868,16 @@ void launch_cascade_cb(const DecodeArgs& a, const SharedJobs& j, hipStream_t st)
     const int64_t sb = (items + rkv::kXcds - 1) / rkv::kXcds * rkv::kXcds;
     int64_t tb = (int64_t)a.splits * a.B * a.hkv;
     tb = (tb + rkv::kXcds - 1) / rkv::kXcds * rkv::kXcds;
-    hipLaunchKernelGGL((decode_cascade_mfma<D, CB>), dim3((unsigned)(sb + tb)), dim3(64), 0, st, a, j,
-                       (int32_t)sb);
+    // Non-temporal tail loads pay when the tails fill the chip (c4, 64/8
+    // heads, 4096 tail slots: 240 -> 230 us) and cost on small, latency-bound
+    // launches (one GPU's 8/1 heads of c4, 512 slots: 37 -> 42 us); the
+    // threshold is the chip's resident waves of this kernel (256 CUs x 8).
+    if (tb >= kStreamTailItems)
+      hipLaunchKernelGGL((decode_cascade_mfma<D, CB, true>), dim3((unsigned)(sb + tb)), dim3(64), 0, st, a, j,
+                         (int32_t)sb);
+    else
+      hipLaunchKernelGGL((decode_cascade_mfma<D, CB, false>), dim3((unsigned)(sb + tb)), dim3(64), 0, st, a, j,
+                         (int32_t)sb);
     return;
   }
   // four shared items per block; tail blocks as the vector kernel's grid
