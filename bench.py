@@ -207,6 +207,10 @@ def gqa_halves(steps, warmup, cfg=None):
             out[name]["cascade"] = dict(kernel="attn_decode_cascade", us=cus, bytes_plan=ph.plan_bytes(),
                                         gbs_plan=ph.plan_bytes() / (cus * 1e-6) / 1e9,
                                         jobs=ph.plan.n_jobs, host_plan_ms=ph.plan_ms)
+            # both decode paths captured into a HIP graph and replayed: the
+            # same kernels without the host side of each call
+            out[name]["graph_us"] = graph_replay_us(ph.attend_plain, steps, warmup)
+            out[name]["cascade"]["graph_us"] = graph_replay_us(ph.attend, steps, warmup)
         del ph
         torch.cuda.empty_cache()
     tot = out["extend"]["us"] + out["extend"]["scatter_us"] + out["decode"]["us"] + out["decode"]["scatter_us"]
@@ -214,6 +218,50 @@ def gqa_halves(steps, warmup, cfg=None):
     out["workload"] = ("llama70b-gqa: 128 requests share a 2048-token prefix; 64 extend 256 tokens (contexts "
                        "2304-8192), 64 decode 1 token (contexts 2049-8192); 64/8 heads, D=128, bf16, 2^20 slots")
     return out
+
+
+def graph_replay_us(fn, steps, warmup):
+    """Mean time of one replay of `fn` captured into a HIP graph
+    (engine.StepGraph), timed like the eager calls: HIP events around each
+    replay on the launch stream, synchronized after each."""
+    import torch
+    from prefix_shared_kv_host_amd.engine import StepGraph
+    g = StepGraph(fn)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    t = []
+    for _ in range(steps):
+        ev[0].record(stream); g.replay(); ev[1].record(stream)
+        torch.cuda.synchronize()
+        t.append(ev[0].elapsed_time(ev[1]))
+    return float(np.mean(t)) * 1e3
+
+
+def step_graph(step, tokens, steps, warmup):
+    """The whole step (both scatters, extend, prefix-shared decode) captured
+    into one HIP graph and replayed, timed like the eager step that `value`
+    reports: wall clock over `steps` replays, synchronized after each, plus
+    HIP events on the launch stream."""
+    import torch
+    from prefix_shared_kv_host_amd.engine import StepGraph
+    g = StepGraph(step)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    t = []
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        ev[0].record(stream); g.replay(); ev[1].record(stream)
+        torch.cuda.synchronize()
+        t.append(ev[0].elapsed_time(ev[1]))
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    return dict(ms_per_step=ms, ms_events=float(np.mean(t)), tokens_per_s=tokens / (ms * 1e-3),
+                note="the same step replayed from a HIP graph (engine.StepGraph); `value` is the eager step")
 
 
 def tp8_share(steps, warmup):
@@ -691,6 +739,7 @@ def main():
         "context": "the pages' up-to-6.4x end-to-end throughput was measured on NVIDIA A10G/A100 "
                    "against other serving systems; it is not comparable to this number",
     }
+    out["step_graph"] = step_graph(step, tokens, args.steps, args.warmup)
     del ext, dec
     torch.cuda.empty_cache()
     out["gqa_llama70b"] = gqa_halves(max(5, args.steps // 2), 3)

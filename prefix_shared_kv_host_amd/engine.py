@@ -52,6 +52,7 @@ class RadixKVCache:
             self.k_pool = torch.empty(shape, dtype=dtype, device=self.device)
             self.v_pool = torch.empty(shape, dtype=dtype, device=self.device)
         self._ws = None
+        self._ws_retired = []
 
     # ---------------------------------------------------------------- host
     def prepare(self, seqs, ld=None) -> Batch:
@@ -87,10 +88,17 @@ class RadixKVCache:
         return o
 
     def workspace(self, B, hq, max_len, num_splits=0, need=None):
+        """Decode workspace of at least `need` bytes (by default what plain
+        decode of this shape needs).  It grows geometrically, and a replaced
+        buffer is kept alive with the cache, since a captured StepGraph may
+        still write into it."""
         if need is None:
             need = rkv.attn_decode_workspace_bytes(B, hq, self.d, max_len, num_splits)
         if self._ws is None or self._ws.numel() * 4 < need:
-            self._ws = torch.empty(max(need // 4, 1), dtype=torch.float32, device=self.device)
+            if self._ws is not None:
+                self._ws_retired.append(self._ws)
+                need = max(need, 2 * self._ws.numel() * 4)
+            self._ws = torch.empty(max((need + 3) // 4, 1), dtype=torch.float32, device=self.device)
         return self._ws
 
     def decode(self, batch: Batch, q, o=None, lse=None, num_splits=0, stream=None):
@@ -123,3 +131,35 @@ class RadixKVCache:
         rkv.attn_decode_cascade(q, self.k_pool, self.v_pool, o, batch.req_to_token, batch.seq_lens,
                                 batch.max_len, plan, ws, lse=lse, stream=stream)
         return o
+
+
+class StepGraph:
+    """A device step (a fixed sequence of library calls on fixed buffers)
+    captured once into a HIP graph and replayed.  A replay skips the host
+    side of every call (argument checks, marshalling, one launch per kernel),
+    which bounds small decode steps: a decode over a few hundred thousand
+    keys runs for tens of microseconds, about what its host side takes.
+
+    `fn` issues the step on the current stream; everything it reads (query
+    rows, tables, the plan, the pools) is read from the buffers it was given
+    when captured, so refresh their contents in place before `replay()`.
+    Sizes that fix a launch grid (batch size, maximum context length, the
+    plan's job and record counts) are frozen at capture: capture again when
+    they change.  `fn` must not allocate; run it once eagerly first (the
+    constructor does, on a side stream) so that caches such as the decode
+    workspace are sized.  Not under RKV_DEBUG=1, whose error check
+    synchronizes the stream."""
+
+    def __init__(self, fn, warmup: int = 1):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(warmup):
+                fn()
+        torch.cuda.current_stream().wait_stream(side)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            fn()
+
+    def replay(self):
+        self.graph.replay()
