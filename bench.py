@@ -702,7 +702,7 @@ def main():
                       tokens_per_s=T_d / ((kern_ms[2] + kern_ms[3]) * 1e-3), scatter_us=kern_ms[2] * 1e3,
                       plan=dict(jobs=pl.n_jobs, records=pl.n_records, tail_splits=pl.tail_splits,
                                 max_members=pl.max_members, tail_chunk=pl.tail_chunk, host_ms=dec.plan_ms,
-                                settings="seg_chunk 256, tail_chunk 768, min_keys 32 (defaults)"))
+                                settings="seg_chunk 256, tail_chunk 768, min_keys 32 (the engine's defaults)"))
     pl_us = float(np.mean(pl_ms)) * 1e3
     decode_plain_obj = dict(kernel="attn_decode (split-KV partial + LSE merge)", us=pl_us,
                             us_cold=float(np.mean(pl_cold)) * 1e3, bytes_logical=Bl,

@@ -110,12 +110,27 @@ class RadixKVCache:
                         batch.max_len, ws, lse=lse, num_splits=num_splits, stream=stream)
         return o
 
-    def cascade_plan(self, batch: Batch, hq, seg_chunk=256, tail_chunk=768, min_keys=32, max_members=None):
+    # Tail chunk of the prefix-shared plan: 768 keys (measured best on the
+    # 32-head and 64/8-head decode batches), halved when the tails would then
+    # give the grouped-head kernel fewer items than the chip has SIMDs (1024):
+    # such launches are latency-bound, and shorter items finish sooner (one
+    # GPU's 8/1 heads of the 64/8 decode batch, 312 tail items at 768 keys:
+    # 36.7 -> 33.9 us at 384).
+    TAIL_CHUNK = 768
+    MIN_TAIL_ITEMS = 1024
+
+    def cascade_plan(self, batch: Batch, hq, seg_chunk=256, tail_chunk=None, min_keys=32, max_members=None):
         """Plans prefix-shared decode from the batch's host tables and copies
-        the plan to the device."""
+        the plan to the device.  tail_chunk None: the rule above."""
         mm = rkv.cascade_max_members(hq, self.hkv, self.d) if max_members is None else max_members
-        plan = rkv.cascade_plan(batch.host["req_to_token"], batch.host["seq_lens"], seg_chunk, tail_chunk,
-                                min_keys, mm)
+        tc = self.TAIL_CHUNK if tail_chunk is None else tail_chunk
+        args = (batch.host["req_to_token"], batch.host["seq_lens"], seg_chunk, tc, min_keys, mm)
+        plan = rkv.cascade_plan(*args)
+        if tail_chunk is None and hq // self.hkv >= 4:
+            tails = batch.host["seq_lens"].astype(np.int64) - plan.tail_begin
+            items = int(((tails + tc - 1) // tc).sum()) * self.hkv
+            if 0 < items < self.MIN_TAIL_ITEMS:
+                plan = rkv.cascade_plan(*args[:3], tc // 2, *args[4:])
         return plan.to(self.device)
 
     def decode_cascade(self, batch: Batch, q, plan=None, o=None, lse=None, stream=None, **plan_args):

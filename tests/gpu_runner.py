@@ -107,7 +107,7 @@ def run(shape, phases, select=lambda i, B: None, num_splits=0, content_device="c
                 o = cache.extend(batch, qd, lse=lse)
             elif cascade is not None:
                 plan = cache.cascade_plan(batch, shape.hq, **cascade)
-                check_plan(plan, otb, **cascade)
+                check_plan(plan, otb, **cascade, hkv=shape.hkv, G=shape.hq // shape.hkv)
                 o = cache.decode_cascade(batch, qd, plan=plan, lse=lse)
             else:
                 o = cache.decode(batch, qd, lse=lse, num_splits=num_splits)
@@ -134,10 +134,22 @@ def run(shape, phases, select=lambda i, B: None, num_splits=0, content_device="c
     return out, cache
 
 
-def check_plan(plan, otb, seg_chunk=256, tail_chunk=768, min_keys=32, max_members=None):
-    """The native prefix-shared plan equals the oracle's, array by array."""
+def check_plan(plan, otb, seg_chunk=256, tail_chunk=None, min_keys=32, max_members=None, hkv=None, G=None):
+    """The native prefix-shared plan equals the oracle's, array by array.
+    tail_chunk None: the engine's default rule, 768 keys, or 384 when the
+    grouped-head tails (G >= 4) would give fewer than 1024 items at 768."""
     from oracle import cascade as ocas
     L = otb["seq_lens"]
+    if tail_chunk is None:
+        tail_chunk = 768
+        if G is not None and G >= 4:
+            rows = [row[: int(L[r])] for r, row in enumerate(otb["req_to_token"])]
+            first = ocas.plan(rows, L, seg_chunk, 768, min_keys, plan.max_members)
+            tails = np.asarray(L, dtype=np.int64) - np.asarray(first["tail_begin"], dtype=np.int64)
+            items = int(((tails + 767) // 768).sum()) * hkv
+            if 0 < items < 1024:
+                tail_chunk = 384
+        assert plan.tail_chunk == tail_chunk, (plan.tail_chunk, tail_chunk)
     ref = ocas.plan([row[: int(L[r])] for r, row in enumerate(otb["req_to_token"])], L, seg_chunk,
                     tail_chunk, min_keys, plan.max_members)
     assert plan.perm.tolist() == ref["perm"]
