@@ -82,6 +82,19 @@ def test_cascade_tree_decode(hq, hkv, d, plan):
 
 
 @pytest.mark.timeout(400)
+@pytest.mark.parametrize("d", [64, 128])
+def test_cascade_streaming_tails(d):
+    """Grouped-head launches with at least 2048 tail slots take the variant
+    whose tail V tiles stream in (non-temporal DMA): 64 requests x 8 kv heads
+    with tails of up to 4 chunks of 768 keys, on both head dims."""
+    shape = configs.Shape(f"cas-stream-{d}", 32, 8, d, "bf16", 1 << 18, 71)
+    phases = tree_decode_workload(seed=d + 71, B=64, max_len=3000)
+    res, _ = G.run(shape, phases, content_device="cpu", cascade=dict(tail_chunk=768),
+                   select=G.sample(3, 12), sparse=True)
+    G.check(res, "bf16", f"cascade streaming tails d{d}")
+
+
+@pytest.mark.timeout(400)
 @pytest.mark.parametrize("name", ["c3", "c3ns"])
 def test_cascade_c3_sampled(name):
     shape, phases = configs.build(name)
