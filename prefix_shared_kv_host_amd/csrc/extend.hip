@@ -511,7 +511,10 @@ __global__ __launch_bounds__(256) void extend_f32(ExtendArgs a) {
     qv[i] = qf[lane + 64 * i] * a.scale_log2e;
     acc[i] = 0.f;
   }
-  float m = -INFINITY, l = 0.f;
+  // l is summed with compensation (Kahan): over a long context a plain
+  // running sum of the weights loses ~sqrt(n) ulps, which lse shows directly
+  // (120k keys: 1.5e-5); lc carries the low-order part lost by each addition
+  float m = -INFINITY, l = 0.f, lc = 0.f;
   const int32_t* row_tab = a.r2t + (int64_t)r * a.ld;
   for (int key = 0; key <= c; ++key) {
     const int32_t slot = row_tab[key];
@@ -529,7 +532,12 @@ __global__ __launch_bounds__(256) void extend_f32(ExtendArgs a) {
     const float mn = fmaxf(m, s);
     const float alpha = exp2f(m - mn);
     const float pw = exp2f(s - mn);
-    l = l * alpha + pw;
+    l *= alpha;
+    lc *= alpha;
+    const float y = pw - lc;
+    const float t = l + y;
+    lc = (t - l) - y;
+    l = t;
 #pragma unroll
     for (int i = 0; i < PER; ++i) acc[i] = fmaf(pw, vf[lane + 64 * i], acc[i] * alpha);
     m = mn;
