@@ -95,3 +95,51 @@ def test_decode_graph_eager_path_matches_oracle():
     phases = [configs.Phase("setup", [f[:-1] for f in full]), configs.Phase("decode", full)]
     res, _ = G.run(shape, phases, content_device="cpu")
     G.check(res, "bf16", "graph batch, eager")
+
+
+def test_full_step_graph_replays_equal_eager():
+    """A whole serving step in one graph: kv_scatter + attn_extend for an
+    extend batch, kv_scatter + prefix-shared decode for a decode batch (the
+    step bench.py times), replayed with the pool rows rewritten each time."""
+    from prefix_shared_kv_host_amd.engine import RadixKVCache, StepGraph
+    hq, hkv, d, seed = 8, 2, 128, 91
+    rng = np.random.default_rng(seed)
+    pool = 1 << 16
+    cache = RadixKVCache(pool, hkv, d, torch.bfloat16, "cuda", configs.free_list(pool, seed))
+    shared = [int(x) for x in rng.integers(0, 32000, 500)]
+    ext_seqs = [shared + [int(x) for x in rng.integers(0, 32000, n)] for n in (1, 17, 64, 130)]
+    dec_full = [shared + [int(x) for x in rng.integers(0, 32000, n)] + [7] for n in (3, 40, 900)]
+    setup = cache.prepare([s_[:-1] for s_ in dec_full])
+    _, k, v = content.batch_rows(seed, [s_[:-1] for s_ in dec_full], setup.host["prefix_lens"], hq, hkv, d,
+                                 torch.bfloat16, "cuda", 1.0, with_q=False)
+    cache.store(setup, k, v)
+    cache.commit(setup)
+    eb = cache.prepare(ext_seqs)
+    eq, ek, ev = content.batch_rows(seed + 1, ext_seqs, eb.host["prefix_lens"], hq, hkv, d, torch.bfloat16,
+                                    "cuda", 1.0)
+    db = cache.prepare(dec_full)
+    dq, dk, dv = content.batch_rows(seed + 2, dec_full, db.host["prefix_lens"], hq, hkv, d, torch.bfloat16,
+                                    "cuda", 1.0)
+    plan = cache.cascade_plan(db, hq, seg_chunk=64, tail_chunk=128, min_keys=8)
+    eo, do = torch.empty_like(eq), torch.empty_like(dq)
+    else_ = torch.empty(eq.shape[0], hq, dtype=torch.float32, device="cuda")
+    dlse = torch.empty(dq.shape[0], hq, dtype=torch.float32, device="cuda")
+
+    def step():
+        cache.store(eb, ek, ev)
+        cache.extend(eb, eq, o=eo, lse=else_)
+        cache.store(db, dk, dv)
+        cache.decode_cascade(db, dq, plan=plan, o=do, lse=dlse)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (eo, else_, do, dlse)]
+    g = StepGraph(step)
+    for rep in range(4):
+        for t in (eo, else_, do, dlse):
+            t.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        for t, r in zip((eo, else_, do, dlse), ref):
+            assert torch.equal(t, r), rep
+    G.log("graph full step: 4 replays equal the eager step")
