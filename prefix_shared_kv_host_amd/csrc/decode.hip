@@ -810,13 +810,36 @@ __global__ __launch_bounds__(64) void decode_merge(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
   float lsum = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float* p = src + (int64_t)s * stride;
-    const float ms = p[D];
+  // partials combined in split order; their loads are issued four splits at
+  // a time, so a request waits about one memory latency per four splits
+  // instead of one per split
+  auto add = [&](float ms, float ls, const float (&v)[PER]) {
     const float f = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-    lsum += p[D + 1] * f;
+    lsum += ls * f;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) acc[i] += p[lane + 64 * i] * f;
+    for (int i = 0; i < PER; ++i) acc[i] += v[i] * f;
+  };
+  constexpr int UNR = 4;
+  int s = 0;
+  for (; s + UNR <= nsplit; s += UNR) {
+    float ms[UNR], ls[UNR], v[UNR][PER];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const float* p = src + (int64_t)(s + u) * stride;
+      ms[u] = p[D];
+      ls[u] = p[D + 1];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) v[u][i] = p[lane + 64 * i];
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) add(ms[u], ls[u], v[u]);
+  }
+  for (; s < nsplit; ++s) {
+    const float* p = src + (int64_t)s * stride;
+    float v[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) v[i] = p[lane + 64 * i];
+    add(p[D], p[D + 1], v);
   }
   const float inv = 1.f / lsum;
   const int64_t ooff = ((int64_t)r * a.hq + head) * D;
