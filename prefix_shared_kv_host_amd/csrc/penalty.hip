@@ -56,7 +56,13 @@ __global__ __launch_bounds__(256) void penalty_admit_kernel(int32_t* __restrict_
     return;
   }
   uint32_t* crow = (uint32_t*)counts + (int64_t)row * vocab;
-  for (int v = threadIdx.x; v < vocab; v += blockDim.x) crow[v] = 0u;
+  // zero the row with 16-byte stores between its unaligned ends
+  const int head = min(vocab, (int)(((16u - ((uint32_t)(uintptr_t)crow & 15u)) & 15u) >> 2));
+  const int nvec = (vocab - head) >> 2;
+  for (int v = threadIdx.x; v < head; v += blockDim.x) crow[v] = 0u;
+  uint4* mid = (uint4*)(crow + head);
+  for (int v = threadIdx.x; v < nvec; v += blockDim.x) mid[v] = make_uint4(0u, 0u, 0u, 0u);
+  for (int v = head + 4 * nvec + (int)threadIdx.x; v < vocab; v += blockDim.x) crow[v] = 0u;
   if (threadIdx.x == 0) n_listed = 0;
   // the barrier's work-group release waits for the zero stores to complete
   // in L2, where the atomic ORs below execute (a device-scope fence would

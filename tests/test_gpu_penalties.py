@@ -76,7 +76,7 @@ def _check_state(st, slot_of, prompts, outputs, V):
 
 
 @pytest.mark.parametrize("dtype,V,B,steps", [(torch.float32, 1000, 24, 12), (torch.bfloat16, 1000, 24, 8),
-                                             (torch.float32, 32000, 64, 6)])
+                                             (torch.float32, 32000, 64, 6), (torch.float32, 1003, 16, 4)])
 def test_penalty_decode_loop(dtype, V, B, steps):
     from prefix_shared_kv_host_amd import rkv
     rng = np.random.default_rng(V + B + steps)
