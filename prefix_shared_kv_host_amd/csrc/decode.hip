@@ -37,7 +37,6 @@
 namespace {
 
 constexpr int kChunk = 768;     // keys per split under the default rule (measured: 512-768 best on MHA, 768 on 64/8 GQA)
-constexpr int kWaves = 4;
 constexpr int kMaxG = 8;        // query heads handled per workgroup
 
 struct DecodeArgs {

@@ -440,7 +440,6 @@ __global__ __launch_bounds__(256, 2) void extend_bf16(ExtendArgs a) {
   // iteration t (K(t+1), V(t) resident): DMA K(t+2), V(t+1) and the slots
   // of tile t+3 while computing; then wait for them and meet at the barrier
   auto iteration = [&](int tile, auto par) {
-    using NPAR = std::integral_constant<int, 1 - decltype(par)::value>;
     // The slot indices of tile t+3 go straight from the table into their
     // LDS stage (wave 0, one 4-byte DMA; they are range-checked where the
     // gathers read them), so no register has to wait for them.  Past the

@@ -154,7 +154,7 @@ struct Logit<uint16_t> {
 // list length (the row stride cap bounds them), and then their counts and
 // logits together, so the dependent gathers overlap.
 template <typename T, bool RECORD>
-__global__ __launch_bounds__(256) void penalty_apply_kernel(void* __restrict__ logits, int64_t ld, int32_t B,
+__global__ __launch_bounds__(256) void penalty_apply_kernel(void* __restrict__ logits, int64_t ld,
                                                            const int32_t* __restrict__ rows, int32_t* counts,
                                                            int32_t* seen, int32_t* seen_len, int32_t* out_len,
                                                            int32_t n_slots, int32_t vocab, int32_t cap,
@@ -284,7 +284,7 @@ extern "C" int rkv_penalty_apply(void* logits, int64_t ld, int32_t dtype, int32_
   if (int rc = rkv::debug_flag(&flag)) return rc;
   hipStream_t st = (hipStream_t)stream;
   auto go = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, dim3((unsigned)B), dim3(256), 0, st, logits, ld, B, rows, counts, seen, seen_len,
+    hipLaunchKernelGGL(kernel, dim3((unsigned)B), dim3(256), 0, st, logits, ld, rows, counts, seen, seen_len,
                        out_len, n_slots, vocab, cap, freq, pres, rep, min_new, stop_indptr, stop_ids, new_tokens, flag);
   };
   if (dtype == RKV_F32) {
