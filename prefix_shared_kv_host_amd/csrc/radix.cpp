@@ -76,14 +76,25 @@ struct rkv_tree {
 
   // ---------------------------------------------------------------- FIFO
   void push(int32_t s) {
-    ring[(head + count) % pool] = s;
+    int64_t i = head + count;
+    if (i >= pool) i -= pool;
+    ring[i] = s;
     ++count;
   }
-  int32_t pop() {
-    int32_t s = ring[head];
-    head = (head + 1) % pool;
-    --count;
-    return s;
+  // pops n slots (n <= count) in FIFO order into each of the non-null
+  // outputs: one or two contiguous runs of the ring
+  void pop_n(int64_t n, int32_t* out_a, int32_t* out_b) {
+    while (n > 0) {
+      const int64_t run = std::min<int64_t>(n, pool - head);
+      if (out_a) std::memcpy(out_a, ring.data() + head, sizeof(int32_t) * (size_t)run);
+      if (out_b) std::memcpy(out_b, ring.data() + head, sizeof(int32_t) * (size_t)run);
+      if (out_a) out_a += run;
+      if (out_b) out_b += run;
+      head += run;
+      if (head == pool) head = 0;
+      count -= run;
+      n -= run;
+    }
   }
 
   // ---------------------------------------------------------------- LRU set
@@ -406,7 +417,7 @@ int rkv_alloc(rkv_tree* t, int64_t n, int32_t* out) {
   rkv::clear_error();
   if (!t || n < 0 || (n > 0 && !out)) return bad("rkv_alloc: bad argument");
   if (t->count < n) return rkv::fail(RKV_ENOSPC, "rkv_alloc: not enough free slots");
-  for (int64_t i = 0; i < n; ++i) out[i] = t->pop();
+  t->pop_n(n, out, nullptr);
   return RKV_OK;
 }
 
@@ -502,12 +513,10 @@ int rkv_batch_prepare(rkv_tree* t, int32_t B, const int32_t* tok, const int64_t*
   int64_t pos = 0;
   for (int32_t r = 0; r < B; ++r) {
     int32_t* row = req_to_token + (int64_t)r * ld;
-    for (int64_t i = prefix_lens[r]; i < seq_lens[r]; ++i) {
-      const int32_t s = t->pop();
-      row[i] = s;
-      new_slots[pos++] = s;
-    }
-    for (int64_t i = seq_lens[r]; i < ld; ++i) row[i] = -1;
+    const int64_t n = (int64_t)seq_lens[r] - prefix_lens[r];
+    t->pop_n(n, row + prefix_lens[r], new_slots + pos);
+    pos += n;
+    std::fill(row + seq_lens[r], row + ld, -1);
     t->matched_total += prefix_lens[r];
     t->prompt_total += seq_lens[r];
   }

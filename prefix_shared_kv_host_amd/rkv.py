@@ -48,6 +48,8 @@ class TokenBatch:
         total = int(self.indptr[-1])
         self.flat = np.fromiter(itertools.chain.from_iterable(seqs), dtype=np.int32, count=total) \
             if total else np.zeros(0, dtype=np.int32)
+        # data addresses, taken once: prepare and commit pass them as they are
+        self.ptrs = (self.flat.ctypes.data, self.indptr.ctypes.data)
 
     def __len__(self):
         return len(self.lens)
@@ -92,9 +94,10 @@ def lib():
         "rkv_stats": (ctypes.c_int, [_vp, c_i64p]),
         "rkv_radix_serialize": (ctypes.c_int, [_vp, c_i64p, _i64, c_i64p]),
         "rkv_free_list": (ctypes.c_int, [_vp, c_i32p, _i64, c_i64p]),
-        "rkv_batch_prepare": (ctypes.c_int, [_vp, _i32, c_i32p, c_i64p, c_i32p, _i64, c_i32p, c_i32p,
-                                             c_i32p, c_i32p, _i64, c_i64p]),
-        "rkv_batch_commit": (ctypes.c_int, [_vp, _i32, c_i32p, c_i64p, c_i32p, _i64, c_i64p]),
+        # the batch calls take integer addresses (marshalling typed pointers
+        # costs microseconds per argument, per batch)
+        "rkv_batch_prepare": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _vp]),
+        "rkv_batch_commit": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _i64, _vp]),
         "rkv_kv_scatter": (ctypes.c_int, [_vp, _vp, _vp, _i64, _vp, _vp, _i64, _i32, _i32, _i32, _vp]),
         "rkv_attn_extend": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _i32, _i64, _i32,
                                            _i32, _i32, _i32, _f32, _i32, _i64, _vp]),
@@ -257,41 +260,68 @@ class Tree:
                 if len(seqs) else np.zeros(0, dtype=np.int32))
         return np.ascontiguousarray(flat, dtype=np.int32), indptr, lens
 
-    def batch_prepare(self, seqs, ld=None):
+    @staticmethod
+    def table_words(B, ld, cap):
+        """int32 words of one buffer holding a batch's tables (see
+        batch_prepare's `out`): req_to_token, prefix_lens, seq_lens,
+        qo_indptr, new_slots, in that order."""
+        return B * ld + 3 * B + 1 + cap
+
+    def batch_prepare(self, seqs, ld=None, out=None):
         """Returns (status, tables); tables hold NumPy arrays req_to_token
         [B, ld], prefix_lens, seq_lens, qo_indptr [B+1], new_slots [T] and
-        nodes.  EBUSY is returned, not raised."""
+        nodes.  EBUSY is returned, not raised.  out: an optional contiguous
+        int32 array of at least table_words(B, ld, sum of lengths) words;
+        the int32 tables are then views of it, in the order table_words
+        lists (so one copy moves them all)."""
         B = len(seqs)
-        flat, indptr, lens = self._flat(seqs)
+        if isinstance(seqs, TokenBatch):
+            lens = seqs.lens
+            pf, pi = seqs.ptrs
+        else:
+            _, _, lens = self._flat(seqs)
+            seqs = TokenBatch(seqs)
+            pf, pi = seqs.ptrs
         if ld is None:
             ld = int(lens.max()) if B else 1
-        r2t = np.empty((max(B, 1), ld), dtype=np.int32)
-        pl = np.empty(max(B, 1), dtype=np.int32)
-        sl = np.empty(max(B, 1), dtype=np.int32)
-        qo = np.zeros(B + 1, dtype=np.int32)
+        Bx = max(B, 1)
         cap = int(lens.sum())
-        ns = np.empty(max(cap, 1), dtype=np.int32)
-        nodes = np.empty(max(B, 1), dtype=np.int64)
-        code = lib().rkv_batch_prepare(
-            self._h, B, flat.ctypes.data_as(c_i32p), indptr.ctypes.data_as(c_i64p),
-            r2t.ctypes.data_as(c_i32p), int(ld), pl.ctypes.data_as(c_i32p), sl.ctypes.data_as(c_i32p),
-            qo.ctypes.data_as(c_i32p), ns.ctypes.data_as(c_i32p), cap, nodes.ctypes.data_as(c_i64p))
+        need = self.table_words(Bx, ld, max(cap, 1))
+        if out is None:
+            buf = np.empty(need, dtype=np.int32)
+        else:
+            if out.dtype != np.int32 or out.ndim != 1 or out.shape[0] < need or not out.flags.c_contiguous:
+                raise RkvError(EINVAL, "batch_prepare: out must be a contiguous int32 array of table_words words")
+            buf = out
+        # word offsets: req_to_token, prefix_lens, seq_lens, qo_indptr (Bx+1), new_slots
+        o1 = Bx * ld
+        o2, o3, o5 = o1 + Bx, o1 + 2 * Bx, o1 + 3 * Bx + 1
+        r2t, pl, sl = buf[:o1].reshape(Bx, ld), buf[o1:o2], buf[o2:o3]
+        qo, ns = buf[o3:o5], buf[o5:o5 + max(cap, 1)]
+        qo[0] = 0
+        nodes = np.empty(Bx, dtype=np.int64)
+        base = buf.ctypes.data
+        code = lib().rkv_batch_prepare(self._h, B, pf, pi, base, int(ld), base + 4 * o1, base + 4 * o2,
+                                       base + 4 * o3, base + 4 * o5, cap, nodes.ctypes.data)
         if code == EBUSY:
             return code, None
         _check(code)
         T = int(qo[B])
-        return OK, dict(req_to_token=r2t[:B], prefix_lens=pl[:B], seq_lens=sl[:B], qo_indptr=qo,
+        return OK, dict(req_to_token=r2t[:B], prefix_lens=pl[:B], seq_lens=sl[:B], qo_indptr=qo[:B + 1],
                         new_slots=ns[:T], nodes=nodes[:B], ld=int(ld))
 
     def batch_commit(self, seqs, req_to_token, nodes) -> int:
         B = len(seqs)
-        flat, indptr, _ = self._flat(seqs)
-        r2t = np.ascontiguousarray(np.asarray(req_to_token, dtype=np.int32))
-        nd = np.ascontiguousarray(np.asarray(nodes, dtype=np.int64))
+        if not isinstance(seqs, TokenBatch):
+            seqs = TokenBatch(seqs)
+        pf, pi = seqs.ptrs
+        r2t = req_to_token if (isinstance(req_to_token, np.ndarray) and req_to_token.dtype == np.int32
+                               and req_to_token.flags.c_contiguous) \
+            else np.ascontiguousarray(np.asarray(req_to_token, dtype=np.int32))
+        nd = nodes if (isinstance(nodes, np.ndarray) and nodes.dtype == np.int64 and nodes.flags.c_contiguous) \
+            else np.ascontiguousarray(np.asarray(nodes, dtype=np.int64))
         ld = r2t.shape[1] if r2t.ndim == 2 and B else 1
-        return _check(lib().rkv_batch_commit(self._h, B, flat.ctypes.data_as(c_i32p),
-                                             indptr.ctypes.data_as(c_i64p), r2t.ctypes.data_as(c_i32p),
-                                             int(ld), nd.ctypes.data_as(c_i64p)))
+        return _check(lib().rkv_batch_commit(self._h, B, pf, pi, r2t.ctypes.data, int(ld), nd.ctypes.data))
 
 
 # ---------------------------------------------------------------------------

@@ -79,3 +79,42 @@ def test_token_batch_equals_lists():
         a.batch_commit(seqs, ta["req_to_token"], ta["nodes"])
         b.batch_commit(tk, tbb["req_to_token"], tbb["nodes"])
         assert a.radix_serialize() == b.radix_serialize()
+
+
+@pytest.mark.parametrize("nreq", [0, 1, 5, 16])
+def test_prepare_into_caller_buffer(nreq):
+    """batch_prepare(out=...) writes every int32 table into one caller buffer
+    of exactly table_words words, in the documented order, and nothing past
+    it (a guard word after the buffer keeps its value); the tables equal
+    those of a call that allocates its own."""
+    from prefix_shared_kv_host_amd import rkv
+    s, phases = configs.build("c2")
+    a = rkv.Tree(4096 * 64, None)
+    b = rkv.Tree(4096 * 64, None)
+    for ph in phases:
+        seqs = [x[:150] for x in ph.seqs[:nreq]]
+        B = len(seqs)
+        ld = max((len(x) for x in seqs), default=1)
+        cap = sum(len(x) for x in seqs)
+        n = rkv.Tree.table_words(max(B, 1), ld, max(cap, 1))
+        store = np.full(n + 1, -7, dtype=np.int32)
+        ca, ta = a.batch_prepare(seqs)
+        cb, tb = b.batch_prepare(rkv.TokenBatch(seqs), ld=ld, out=store[:n])
+        assert ca == cb == rkv.OK
+        assert store[n] == -7
+        for key in ("req_to_token", "prefix_lens", "seq_lens", "qo_indptr", "new_slots"):
+            assert np.array_equal(ta[key], tb[key]), key
+        Bx = max(B, 1)
+        T = int(tb["qo_indptr"][B])
+        flat = np.concatenate([store[:Bx * ld].reshape(Bx, ld)[:B].ravel(), store[Bx * ld:Bx * ld + Bx][:B],
+                               store[Bx * ld + Bx:Bx * ld + 2 * Bx][:B],
+                               store[Bx * ld + 2 * Bx:Bx * ld + 3 * Bx + 1][:B + 1],
+                               store[Bx * ld + 3 * Bx + 1:][:T]])
+        ref = np.concatenate([ta["req_to_token"].ravel(), ta["prefix_lens"], ta["seq_lens"],
+                              ta["qo_indptr"], ta["new_slots"]])
+        assert np.array_equal(flat, ref)
+        a.batch_commit(seqs, ta["req_to_token"], ta["nodes"])
+        b.batch_commit(seqs, tb["req_to_token"], tb["nodes"])
+        assert a.radix_serialize() == b.radix_serialize()
+    with pytest.raises(rkv.RkvError):
+        b.batch_prepare([[1, 2, 3]], out=np.zeros(2, dtype=np.int32))
