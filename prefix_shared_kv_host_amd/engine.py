@@ -60,18 +60,24 @@ class RadixKVCache:
         once here either way and reused by commit)."""
         if not isinstance(seqs, rkv.TokenBatch):
             seqs = rkv.TokenBatch(seqs)
-        code, tb = self.tree.batch_prepare(seqs, ld)
+        B = len(seqs)
+        if ld is None:
+            ld = int(seqs.lens.max()) if B else 1
+        # all int32 tables land in one pinned buffer and go up in one copy
+        # (torch's pinned-block cache keeps the block until the copy is done)
+        lay = rkv.Tree.table_layout(B, ld, int(seqs.lens.sum()))
+        pinned = torch.empty(lay[-1], dtype=torch.int32, pin_memory=True)
+        code, tb = self.tree.batch_prepare(seqs, ld, out=pinned.numpy())
         if code != rkv.OK:
             raise rkv.RkvError(code, "batch_prepare: eviction cannot free enough slots")
-
-        def up(a):
-            return torch.from_numpy(np.ascontiguousarray(a)).pin_memory().to(self.device, non_blocking=True)
-
+        dev = pinned.to(self.device, non_blocking=True)
+        T = int(tb["qo_indptr"][B])
         n = tb["seq_lens"].astype(np.int64) - tb["prefix_lens"]
-        return Batch(seqs=seqs, host=tb, req_to_token=up(tb["req_to_token"]), qo_indptr=up(tb["qo_indptr"]),
-                     prefix_lens=up(tb["prefix_lens"]), seq_lens=up(tb["seq_lens"]),
-                     new_slots=up(tb["new_slots"]), max_new=int(n.max()) if len(n) else 0,
-                     max_len=int(tb["seq_lens"].max()) if len(n) else 0, total_new=int(tb["qo_indptr"][-1]))
+        return Batch(seqs=seqs, host=tb, req_to_token=dev[:lay[1]].view(-1, ld)[:B],
+                     prefix_lens=dev[lay[1]:lay[1] + B], seq_lens=dev[lay[2]:lay[2] + B],
+                     qo_indptr=dev[lay[3]:lay[3] + B + 1], new_slots=dev[lay[4]:lay[4] + T],
+                     max_new=int(n.max()) if len(n) else 0,
+                     max_len=int(tb["seq_lens"].max()) if len(n) else 0, total_new=T)
 
     def commit(self, batch: Batch):
         self.tree.batch_commit(batch.seqs, batch.host["req_to_token"], batch.host["nodes"])

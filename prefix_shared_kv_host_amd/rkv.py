@@ -261,11 +261,19 @@ class Tree:
         return np.ascontiguousarray(flat, dtype=np.int32), indptr, lens
 
     @staticmethod
+    def table_layout(B, ld, cap):
+        """Word offsets of the int32 tables of a B-request batch in one
+        buffer (batch_prepare's `out`): (req_to_token [B*ld], prefix_lens [B],
+        seq_lens [B], qo_indptr [B+1], new_slots [cap], end).  B and cap are
+        taken as at least 1."""
+        Bx, cx = max(B, 1), max(cap, 1)
+        o1 = Bx * ld
+        return 0, o1, o1 + Bx, o1 + 2 * Bx, o1 + 3 * Bx + 1, o1 + 3 * Bx + 1 + cx
+
+    @staticmethod
     def table_words(B, ld, cap):
-        """int32 words of one buffer holding a batch's tables (see
-        batch_prepare's `out`): req_to_token, prefix_lens, seq_lens,
-        qo_indptr, new_slots, in that order."""
-        return B * ld + 3 * B + 1 + cap
+        """int32 words of one buffer holding a batch's tables."""
+        return Tree.table_layout(B, ld, cap)[-1]
 
     def batch_prepare(self, seqs, ld=None, out=None):
         """Returns (status, tables); tables hold NumPy arrays req_to_token
@@ -286,18 +294,15 @@ class Tree:
             ld = int(lens.max()) if B else 1
         Bx = max(B, 1)
         cap = int(lens.sum())
-        need = self.table_words(Bx, ld, max(cap, 1))
+        _, o1, o2, o3, o5, need = self.table_layout(B, ld, cap)
         if out is None:
             buf = np.empty(need, dtype=np.int32)
         else:
             if out.dtype != np.int32 or out.ndim != 1 or out.shape[0] < need or not out.flags.c_contiguous:
                 raise RkvError(EINVAL, "batch_prepare: out must be a contiguous int32 array of table_words words")
             buf = out
-        # word offsets: req_to_token, prefix_lens, seq_lens, qo_indptr (Bx+1), new_slots
-        o1 = Bx * ld
-        o2, o3, o5 = o1 + Bx, o1 + 2 * Bx, o1 + 3 * Bx + 1
         r2t, pl, sl = buf[:o1].reshape(Bx, ld), buf[o1:o2], buf[o2:o3]
-        qo, ns = buf[o3:o5], buf[o5:o5 + max(cap, 1)]
+        qo, ns = buf[o3:o5], buf[o5:need]
         qo[0] = 0
         nodes = np.empty(Bx, dtype=np.int64)
         base = buf.ctypes.data
