@@ -192,6 +192,24 @@ int rkv_batch_prepare(rkv_tree* t, int32_t B, const int32_t* tok, const int64_t*
 int rkv_batch_commit(rkv_tree* t, int32_t B, const int32_t* tok, const int64_t* tok_indptr,
                      const int32_t* req_to_token, int64_t ld, const int64_t* nodes);
 
+/* Decode continuation of a prepared batch that is not yet committed (its
+ * nodes still locked): one more position per request, without matching the
+ * history again.  The pages' walkthrough (unite.ai, "SGLang: Efficient
+ * Execution of Structured Language Model Programs", section "SGLang: Modelo
+ * de programacion y metodologia", Step 3) caches a finished turn, answer
+ * included, as one new node; here the generated tokens therefore enter the
+ * tree only at rkv_batch_commit, and each step needs just one new slot per
+ * request.  If fewer than B slots are free, evict the difference (RKV_EBUSY
+ * if that fails: no slot popped, no table entry written; leaves evicted on
+ * the way stay evicted).  Then pop B slots in FIFO order and for r = 0..B-1:
+ * req_to_token[r, seq_lens[r]] = new_slots[r], seq_lens[r] += 1.
+ * req_to_token [B, ld] and seq_lens [B] are the caller's host tables from
+ * rkv_batch_prepare (updated in place); every seq_lens[r] must be in
+ * [1, ld - 1] (else RKV_EINVAL, nothing changed).  new_slots [B] is written.
+ * Commit later with the extended token sequences.  B = 0 is a no-op. */
+int rkv_batch_append(rkv_tree* t, int32_t B, int32_t* req_to_token, int64_t ld, int32_t* seq_lens,
+                     int32_t* new_slots);
+
 /* ------------------------------------------------------------------------
  * Device: every pointer below is a device pointer owned by the caller, 16-byte
  * aligned, tensors contiguous.  Calls are asynchronous on `stream` (a
@@ -216,6 +234,15 @@ int rkv_batch_commit(rkv_tree* t, int32_t B, const int32_t* tok, const int64_t* 
 int rkv_kv_scatter(const void* k_new, const void* v_new, const int32_t* slots, int64_t T,
                    void* k_pool, void* v_pool, int64_t pool_slots, int32_t hkv, int32_t d,
                    int32_t dtype, void* stream);
+
+/* Device side of rkv_batch_append, for a req_to_token / seq_lens pair kept
+ * on the device across decode steps (only the B new slot ids cross PCIe per
+ * step): for r in [0, B), req_to_token[r, seq_lens[r]] = new_slots[r] and
+ * seq_lens[r] += 1.  All three are int32 device arrays (4-byte alignment
+ * suffices).  A row whose seq_lens[r] is outside [0, ld) is left as it is
+ * (with RKV_DEBUG=1 the call then returns RKV_EINVAL).  B = 0 is a no-op. */
+int rkv_table_append(int32_t* req_to_token, int64_t ld, int32_t* seq_lens, const int32_t* new_slots,
+                     int32_t B, void* stream);
 
 /* Extend (prefill over a cached prefix).  Request r has p_r = prefix_lens[r]
  * cached tokens and n_r = qo_indptr[r+1] - qo_indptr[r] new ones, whose

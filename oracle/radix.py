@@ -38,7 +38,13 @@ implementations can agree bit for bit:
   * batch_prepare matches each request capped at its length minus one (so
     every request computes at least its last token), locks the stop node,
     evicts if the free list is short, pops all new slots and fills the index
-    tables; batch_commit inserts each full sequence and unlocks.
+    tables; batch_commit inserts each full sequence and unlocks;
+  * batch_append continues a prepared, uncommitted batch by one decode
+    position per request without matching again: a finished turn, answer
+    included, becomes one node (Step 3), so generated tokens reach the tree
+    only at the commit.  It evicts if fewer slots than requests are free
+    (EBUSY if it cannot), pops one slot per request in request order, writes
+    it after the row's last entry and extends the length.
 
 The implementation is deliberately naive: children are a Python list scanned
 linearly, the LRU leaf is found by scanning every node.
@@ -275,6 +281,27 @@ class OracleTree:
             self.prompt_total += lens[r]
         return OK, dict(req_to_token=r2t, prefix_lens=pref, seq_lens=lens,
                         qo_indptr=indptr, new_slots=new, nodes=nodes)
+
+    def batch_append(self, req_to_token, seq_lens):
+        """One more position per request of a prepared batch; req_to_token
+        (rows of length ld) and seq_lens are updated in place.  Returns
+        (status, new_slots)."""
+        B = len(seq_lens)
+        if B == 0:
+            return OK, []
+        ld = len(req_to_token[0])
+        if any(L < 1 or L >= ld for L in seq_lens):
+            return EINVAL, None
+        if len(self.fifo) < B:
+            st, _ = self.evict(B - len(self.fifo))
+            if st != OK:
+                return EBUSY, None
+        st, new = self.alloc(B)
+        assert st == OK
+        for r in range(B):
+            req_to_token[r][seq_lens[r]] = new[r]
+            seq_lens[r] += 1
+        return OK, new
 
     def batch_commit(self, seqs, req_to_token, nodes):
         for r, s in enumerate(seqs):

@@ -549,4 +549,26 @@ int rkv_batch_commit(rkv_tree* t, int32_t B, const int32_t* tok, const int64_t* 
   return RKV_OK;
 }
 
+int rkv_batch_append(rkv_tree* t, int32_t B, int32_t* req_to_token, int64_t ld, int32_t* seq_lens,
+                     int32_t* new_slots) {
+  rkv::clear_error();
+  if (!t || B < 0) return bad("rkv_batch_append: bad argument");
+  if (B == 0) return RKV_OK;
+  if (!req_to_token || !seq_lens || !new_slots || ld < 2) return bad("rkv_batch_append: bad argument");
+  for (int32_t r = 0; r < B; ++r)
+    if (seq_lens[r] < 1 || (int64_t)seq_lens[r] >= ld)
+      return bad("rkv_batch_append: every length must be in [1, ld - 1]");
+  if (t->count < B) {
+    int64_t freed = 0;
+    if (t->do_evict(B - t->count, &freed) != RKV_OK)
+      return rkv::fail(RKV_EBUSY, "rkv_batch_append: eviction cannot free enough slots");
+  }
+  t->pop_n(B, new_slots, nullptr);
+  for (int32_t r = 0; r < B; ++r) {
+    req_to_token[(int64_t)r * ld + seq_lens[r]] = new_slots[r];
+    ++seq_lens[r];
+  }
+  return RKV_OK;
+}
+
 }  // extern "C"

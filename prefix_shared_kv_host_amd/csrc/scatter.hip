@@ -41,7 +41,38 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(const uint4* __restrict
   }
 }
 
+// One lane per request: the decode step's new slot goes after the row's last
+// entry and the length grows by one.
+__global__ __launch_bounds__(256) void table_append_kernel(int32_t* __restrict__ r2t, int64_t ld,
+                                                           int32_t* __restrict__ seq_lens,
+                                                           const int32_t* __restrict__ new_slots, int32_t B,
+                                                           int* err) {
+  const int32_t r = (int32_t)(blockIdx.x * blockDim.x + threadIdx.x);
+  if (r >= B) return;
+  const int32_t L = seq_lens[r];
+  if (L < 0 || (int64_t)L >= ld) {
+    rkv::raise_flag(err);
+    return;
+  }
+  r2t[(int64_t)r * ld + L] = new_slots[r];
+  seq_lens[r] = L + 1;
+}
+
 }  // namespace
+
+extern "C" int rkv_table_append(int32_t* req_to_token, int64_t ld, int32_t* seq_lens, const int32_t* new_slots,
+                                int32_t B, void* stream) {
+  rkv::clear_error();
+  if (B < 0 || ld < 1) return rkv::fail(RKV_EINVAL, "rkv_table_append: bad sizes");
+  if (B == 0) return RKV_OK;
+  if (!req_to_token || !seq_lens || !new_slots) return rkv::fail(RKV_EINVAL, "rkv_table_append: NULL pointer");
+  int* flag = nullptr;
+  if (int rc = rkv::debug_flag(&flag)) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  hipLaunchKernelGGL(table_append_kernel, dim3((unsigned)((B + 255) / 256)), dim3(256), 0, st, req_to_token, ld,
+                     seq_lens, new_slots, B, flag);
+  return rkv::finish_launch("rkv_table_append", st, flag);
+}
 
 extern "C" int rkv_kv_scatter(const void* k_new, const void* v_new, const int32_t* slots, int64_t T,
                               void* k_pool, void* v_pool, int64_t pool_slots, int32_t hkv, int32_t d,

@@ -33,6 +33,7 @@ class Batch:
     max_new: int
     max_len: int
     total_new: int
+    uploaded: object = None     # event after the tables' upload (the host tables are its source)
 
 
 class RadixKVCache:
@@ -71,16 +72,45 @@ class RadixKVCache:
         if code != rkv.OK:
             raise rkv.RkvError(code, "batch_prepare: eviction cannot free enough slots")
         dev = pinned.to(self.device, non_blocking=True)
+        uploaded = torch.cuda.Event()
+        uploaded.record()
         T = int(tb["qo_indptr"][B])
         n = tb["seq_lens"].astype(np.int64) - tb["prefix_lens"]
         return Batch(seqs=seqs, host=tb, req_to_token=dev[:lay[1]].view(-1, ld)[:B],
                      prefix_lens=dev[lay[1]:lay[1] + B], seq_lens=dev[lay[2]:lay[2] + B],
                      qo_indptr=dev[lay[3]:lay[3] + B + 1], new_slots=dev[lay[4]:lay[4] + T],
                      max_new=int(n.max()) if len(n) else 0,
-                     max_len=int(tb["seq_lens"].max()) if len(n) else 0, total_new=T)
+                     max_len=int(tb["seq_lens"].max()) if len(n) else 0, total_new=T, uploaded=uploaded)
 
-    def commit(self, batch: Batch):
-        self.tree.batch_commit(batch.seqs, batch.host["req_to_token"], batch.host["nodes"])
+    def append(self, batch: Batch) -> Batch:
+        """Decode continuation of a prepared, uncommitted batch: one more
+        position per request, without matching the histories again.  The
+        host tables grow by rkv_batch_append, the device ones by
+        rkv_table_append, so only the B new slot ids cross PCIe.  Updates
+        and returns `batch` (new_slots then holds the step's B slots, for
+        store); the batch must have been prepared with room in ld.  Commit
+        with the extended sequences: commit(batch, seqs)."""
+        if batch.uploaded is not None:
+            batch.uploaded.synchronize()     # the prepare's upload reads the host tables
+            batch.uploaded = None
+        B = int(batch.host["seq_lens"].shape[0])
+        pinned = torch.empty(max(B, 1), dtype=torch.int32, pin_memory=True)
+        code, _ = self.tree.batch_append(batch.host["req_to_token"], batch.host["seq_lens"], out=pinned.numpy())
+        if code != rkv.OK:
+            raise rkv.RkvError(code, "batch_append: eviction cannot free enough slots")
+        dev = pinned[:B].to(self.device, non_blocking=True)
+        rkv.table_append(batch.req_to_token, batch.seq_lens, dev)
+        batch.new_slots = dev
+        batch.max_len += 1
+        batch.max_new = 1 if B else 0
+        batch.total_new = B
+        return batch
+
+    def commit(self, batch: Batch, seqs=None):
+        """Inserts the batch's sequences (`seqs` when the batch was extended
+        by append) and unlocks their paths."""
+        self.tree.batch_commit(batch.seqs if seqs is None else seqs, batch.host["req_to_token"],
+                               batch.host["nodes"])
 
     # ---------------------------------------------------------------- device
     def store(self, batch: Batch, k_new, v_new, stream=None):

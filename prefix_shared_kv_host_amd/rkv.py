@@ -32,7 +32,8 @@ EXPORTS = (
     "rkv_batch_commit", "rkv_kv_scatter", "rkv_attn_extend", "rkv_attn_decode_workspace_bytes",
     "rkv_attn_decode", "rkv_radix_peek", "rkv_schedule", "rkv_cascade_plan",
     "rkv_attn_decode_cascade_workspace_bytes", "rkv_attn_decode_cascade", "rkv_penalty_admit",
-    "rkv_penalty_accumulate", "rkv_penalty_apply", "rkv_image_keys",
+    "rkv_penalty_accumulate", "rkv_penalty_apply", "rkv_image_keys", "rkv_batch_append",
+    "rkv_table_append",
 )
 
 
@@ -98,6 +99,8 @@ def lib():
         # costs microseconds per argument, per batch)
         "rkv_batch_prepare": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _vp]),
         "rkv_batch_commit": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _i64, _vp]),
+        "rkv_batch_append": (ctypes.c_int, [_vp, _i32, _vp, _i64, _vp, _vp]),
+        "rkv_table_append": (ctypes.c_int, [_vp, _i64, _vp, _vp, _i32, _vp]),
         "rkv_kv_scatter": (ctypes.c_int, [_vp, _vp, _vp, _i64, _vp, _vp, _i64, _i32, _i32, _i32, _vp]),
         "rkv_attn_extend": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _i32, _i64, _i32,
                                            _i32, _i32, _i32, _f32, _i32, _i64, _vp]),
@@ -328,6 +331,28 @@ class Tree:
         ld = r2t.shape[1] if r2t.ndim == 2 and B else 1
         return _check(lib().rkv_batch_commit(self._h, B, pf, pi, r2t.ctypes.data, int(ld), nd.ctypes.data))
 
+    def batch_append(self, req_to_token, seq_lens, out=None):
+        """Decode continuation (rkv_batch_append): one new slot per request
+        of a prepared, uncommitted batch, written into the host tables
+        req_to_token [B, ld] and seq_lens [B] in place (contiguous int32
+        arrays, e.g. the views batch_prepare returned).  Returns (status,
+        new_slots [B]); EBUSY is returned, not raised."""
+        for a in (req_to_token, seq_lens):
+            if not (isinstance(a, np.ndarray) and a.dtype == np.int32 and a.flags.c_contiguous):
+                raise RkvError(EINVAL, "batch_append: tables must be contiguous int32 arrays")
+        B = int(seq_lens.shape[0])
+        if req_to_token.ndim != 2 or req_to_token.shape[0] != B:
+            raise RkvError(EINVAL, "batch_append: req_to_token must be [B, ld]")
+        ns = np.empty(max(B, 1), dtype=np.int32) if out is None else out
+        if ns.dtype != np.int32 or ns.shape[0] < B or not ns.flags.c_contiguous:
+            raise RkvError(EINVAL, "batch_append: out must be a contiguous int32 array of B entries")
+        code = lib().rkv_batch_append(self._h, B, req_to_token.ctypes.data, int(req_to_token.shape[1]),
+                                      seq_lens.ctypes.data, ns.ctypes.data)
+        if code == EBUSY:
+            return code, None
+        _check(code)
+        return OK, ns[:B]
+
 
 # ---------------------------------------------------------------------------
 # device entry points (torch tensors in, pointers out)
@@ -366,6 +391,21 @@ def kv_scatter(k_new, v_new, slots, k_pool, v_pool, stream=None):
     return _check(lib().rkv_kv_scatter(_ptr(k_new), _ptr(v_new), _ptr(slots), int(slots.shape[0]),
                                        _ptr(k_pool), _ptr(v_pool), int(P), int(hkv), int(d),
                                        _dtype_code(k_pool), _stream(stream)))
+
+
+def table_append(req_to_token, seq_lens, new_slots, stream=None):
+    """Device tables: req_to_token[r, seq_lens[r]] = new_slots[r] and
+    seq_lens[r] += 1 for every request r (int32 GPU tensors)."""
+    import torch
+    _need_cuda(req_to_token, seq_lens, new_slots)
+    for t in (req_to_token, seq_lens, new_slots):
+        if t.dtype != torch.int32:
+            raise RkvError(EINVAL, "table_append takes int32 tensors")
+    B = int(seq_lens.shape[0])
+    if req_to_token.dim() != 2 or req_to_token.shape[0] != B or new_slots.shape[0] < B:
+        raise RkvError(EINVAL, "table_append: req_to_token must be [B, ld], new_slots [B]")
+    return _check(lib().rkv_table_append(_ptr(req_to_token), int(req_to_token.shape[1]), _ptr(seq_lens),
+                                         _ptr(new_slots), B, _stream(stream)))
 
 
 def attn_extend(q, k_pool, v_pool, o, req_to_token, qo_indptr, prefix_lens, max_new, lse=None,

@@ -1,5 +1,7 @@
 """Adapter giving the native tree (through the ctypes binding) the same
 Python API as the oracle tree, for lockstep comparisons."""
+import numpy as np
+
 from prefix_shared_kv_host_amd import rkv
 
 
@@ -48,3 +50,18 @@ class NativeTree:
 
     def batch_commit(self, seqs, req_to_token, nodes):
         return self.t.batch_commit(seqs, req_to_token, nodes)
+
+    def batch_append(self, req_to_token, seq_lens):
+        """Same in-place list semantics as the oracle's batch_append."""
+        r2t = np.ascontiguousarray(np.asarray(req_to_token, dtype=np.int32))
+        sl = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+        try:
+            code, ns = self.t.batch_append(r2t, sl)
+        except rkv.RkvError as e:
+            return e.code, None
+        if ns is None:
+            return code, None
+        for r in range(len(seq_lens)):
+            req_to_token[r][:] = r2t[r].tolist()
+            seq_lens[r] = int(sl[r])
+        return code, ns.tolist()
