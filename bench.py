@@ -298,6 +298,55 @@ def chat_pipeline(name):
     return out
 
 
+def decode_loop_host(steps=16):
+    """Per-step cost outside the kernels of a decode loop over the radix-tree
+    decode batch (256 requests of 512-4096 tokens): matching every history
+    again each step (prepare + commit of the grown batch, the whole token
+    table uploaded) against continuing the prepared batch (append: one slot
+    per request on the host, B slot ids uploaded, the device table grown in
+    place by rkv_table_append; one commit at the end, counted).  No attention
+    runs: this is the host tree and table traffic a step adds."""
+    import torch
+    from inputs import configs
+    from prefix_shared_kv_host_amd import rkv
+    from prefix_shared_kv_host_amd.engine import RadixKVCache
+
+    s, phases = configs.build("c3")
+    dec = phases[-1]
+    B = len(dec.seqs)
+    ld = max(len(x) for x in dec.seqs) + steps + 1
+    grown = [[list(x) for x in dec.seqs]]
+    for k in range(steps):
+        grown.append([x + [1_000_000 + 1000 * k + i] for i, x in enumerate(grown[-1])])
+    toks = [rkv.TokenBatch(g) for g in grown]           # token arrays, as a server holds them
+    out = dict(requests=B, steps=steps, ld=ld)
+    for mode in ("rematch", "append"):
+        # the tables do not depend on the head shape: one 64-wide kv head keeps the pool small
+        cache = RadixKVCache(s.pool, 1, 64, torch.bfloat16, "cuda", configs.free_list(s.pool, s.seed),
+                             poison=False)
+        for ph in phases[:-1]:
+            cache.commit(cache.prepare(ph.seqs))
+        b = cache.prepare(toks[0], ld)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        if mode == "rematch":
+            cache.commit(b)
+            for k in range(1, steps + 1):
+                b = cache.prepare(toks[k], ld)
+                cache.commit(b)
+        else:
+            for k in range(1, steps + 1):
+                cache.append(b)
+            cache.commit(b, toks[steps])
+        torch.cuda.synchronize()
+        out[f"{mode}_ms_per_step"] = (time.perf_counter() - t0) * 1e3 / steps
+        del cache, b
+        torch.cuda.empty_cache()
+    out["rematch_upload_bytes_per_step"] = 4 * (B * ld + 3 * B + 1 + B)
+    out["append_upload_bytes_per_step"] = 4 * B
+    return out
+
+
 def replay(s, phases):
     """Times batches end to end: host radix prepare/commit, table upload,
     kv_scatter and attn_extend for every batch."""
@@ -745,6 +794,7 @@ def main():
     out["gqa_llama70b"] = gqa_halves(max(5, args.steps // 2), 3)
     out["tp8_share"] = tp8_share(max(5, args.steps // 2), 3)
     out["chat_pipeline"] = [chat_pipeline("c5"), chat_pipeline("c5e")]
+    out["decode_loop_host"] = decode_loop_host()
     out["cache_aware_scheduling"] = queue_orders()
     out["sampling_penalties"] = sampling_penalties()
     out["multimodal"] = multimodal_replay()
