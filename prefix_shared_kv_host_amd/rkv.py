@@ -286,13 +286,10 @@ class Tree:
         the int32 tables are then views of it, in the order table_words
         lists (so one copy moves them all)."""
         B = len(seqs)
-        if isinstance(seqs, TokenBatch):
-            lens = seqs.lens
-            pf, pi = seqs.ptrs
-        else:
-            _, _, lens = self._flat(seqs)
+        if not isinstance(seqs, TokenBatch):
             seqs = TokenBatch(seqs)
-            pf, pi = seqs.ptrs
+        lens = seqs.lens
+        pf, pi = seqs.ptrs
         if ld is None:
             ld = int(lens.max()) if B else 1
         Bx = max(B, 1)
