@@ -347,6 +347,62 @@ def decode_loop_host(steps=16):
     return out
 
 
+def decode_loop(steps=33):
+    """End-to-end decode loop over the radix-tree decode batch (256 requests
+    of 512-4096 tokens, 32 heads, D=128, bf16): each step grows the batch by
+    append, plans prefix-shared decode on the host, stores the step's new K/V
+    and runs the prefix-shared decode; nothing waits for the GPU inside the
+    loop, so the host work of step k+1 overlaps the kernels of step k.  The
+    steps' q/k/v stand for the model's projections and are generated before
+    timing; the first step (the prepare's own token) is not timed."""
+    import torch
+    from inputs import configs, content
+    from prefix_shared_kv_host_amd.engine import RadixKVCache
+
+    s, phases = configs.build("c3")
+    dt = content.torch_dtype(s.dtype)
+    cache = RadixKVCache(s.pool, s.hkv, s.d, dt, "cuda", configs.free_list(s.pool, s.seed), poison=False)
+    for ph in phases[:-1]:
+        b = cache.prepare(ph.seqs)
+        _, k, v = content.batch_rows(s.seed, ph.seqs, b.host["prefix_lens"], s.hq, s.hkv, s.d, dt, "cuda",
+                                     with_q=False)
+        cache.store(b, k, v)
+        cache.commit(b)
+        del k, v
+    dec = phases[-1]
+    B = len(dec.seqs)
+    b = cache.prepare(dec.seqs, max(len(x) for x in dec.seqs) + steps + 1)
+    g = torch.Generator(device="cuda").manual_seed(s.seed)
+    qkv = [tuple(torch.randn(B, h, s.d, device="cuda", generator=g).to(dt) for h in (s.hq, s.hkv, s.hkv))
+           for _ in range(steps)]
+    o = torch.empty(B, s.hq, s.d, dtype=dt, device="cuda")
+    cache.store(b, qkv[0][1], qkv[0][2])
+    cache.decode_cascade(b, qkv[0][0], plan=cache.cascade_plan(b, s.hq), o=o)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = []
+    t0 = time.perf_counter()
+    for k in range(1, steps):
+        cache.append(b)
+        plan = cache.cascade_plan(b, s.hq)
+        q, kn, vn = qkv[k]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        cache.store(b, kn, vn)
+        cache.decode_cascade(b, q, plan=plan, o=o)
+        e1.record(stream)
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    n = steps - 1
+    dev_ms = sum(a.elapsed_time(c) for a, c in ev) / n
+    out = dict(requests=B, steps=n, ms_per_step=wall * 1e3 / n, device_ms_per_step=dev_ms,
+               tokens_per_s=B * n / wall, final_max_len=int(b.max_len))
+    del cache, b, qkv, o
+    torch.cuda.empty_cache()
+    return out
+
+
 def replay(s, phases):
     """Times batches end to end: host radix prepare/commit, table upload,
     kv_scatter and attn_extend for every batch."""
@@ -795,6 +851,7 @@ def main():
     out["tp8_share"] = tp8_share(max(5, args.steps // 2), 3)
     out["chat_pipeline"] = [chat_pipeline("c5"), chat_pipeline("c5e")]
     out["decode_loop_host"] = decode_loop_host()
+    out["decode_loop"] = decode_loop()
     out["cache_aware_scheduling"] = queue_orders()
     out["sampling_penalties"] = sampling_penalties()
     out["multimodal"] = multimodal_replay()

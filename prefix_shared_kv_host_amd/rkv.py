@@ -453,11 +453,25 @@ class CascadePlan:
         self.dev = None
 
     def to(self, device):
-        """Copies the arrays to `device` (int32 torch tensors); returns self."""
+        """Copies the arrays to `device` as int32 views of one buffer, each
+        starting on a 16-byte boundary, sent by one asynchronous copy from
+        pinned memory (a pageable copy would wait for the stream's earlier
+        work, so a decode loop could not plan step k+1 while step k runs);
+        returns self."""
         import torch
-        self.dev = {k: torch.from_numpy(np.ascontiguousarray(v)).to(device)
-                    for k, v in (("perm", self.perm), ("rec_indptr", self.rec_indptr),
-                                 ("tail_begin", self.tail_begin), ("jobs", self.jobs.reshape(-1)))}
+        parts = (("perm", self.perm), ("rec_indptr", self.rec_indptr), ("tail_begin", self.tail_begin),
+                 ("jobs", self.jobs.reshape(-1)))
+        spans, off = {}, 0
+        for k, v in parts:
+            spans[k] = (off, int(v.size))
+            off += (int(v.size) + 3) // 4 * 4
+        pinned = torch.empty(max(off, 4), dtype=torch.int32, pin_memory=True)
+        h = pinned.numpy()
+        for k, v in parts:
+            o, n = spans[k]
+            h[o:o + n] = v.reshape(-1)
+        dev = pinned.to(device, non_blocking=True)
+        self.dev = {k: dev[o:o + n] for k, (o, n) in spans.items()}
         return self
 
 
