@@ -259,10 +259,19 @@ int rkv_table_append(int32_t* req_to_token, int64_t ld, int32_t* seq_lens, const
  * softmax, softmax weights rounded to bf16 for PV, o rounded to bf16 (RNE).
  * The row sums that normalize o (and give lse) are sums of those same
  * rounded weights, so bf16 lse is within ln(1 + 2^-8) of the exact value.
- * f32: fp32 arithmetic throughout.  B = 0 or total_new = 0 is a no-op. */
+ * f32: fp32 arithmetic throughout.  B = 0 or total_new = 0 is a no-op.
+ * req_order (nullable, int32 [B], device): a permutation of the requests in
+ * which the bf16 path hands out work (each request's row tiles still in
+ * ascending order); it changes only the schedule (every output is
+ * bit-identical to NULL's).
+ * Longest first shortens ragged batches, whose launch otherwise ends on a
+ * long request started late.  An entry outside [0, B) is skipped; a
+ * repeated or missing request leaves rows written twice or not at all.  The
+ * f32 path ignores it. */
 int rkv_attn_extend(const void* q, const void* k_pool, const void* v_pool, void* o, float* lse,
                     const int32_t* req_to_token, int64_t ld, const int32_t* qo_indptr,
-                    const int32_t* prefix_lens, int32_t B, int64_t total_new, int32_t max_new,
+                    const int32_t* prefix_lens, const int32_t* req_order, int32_t B,
+                    int64_t total_new, int32_t max_new,
                     int32_t hq, int32_t hkv, int32_t d, float sm_scale, int32_t dtype,
                     int64_t pool_slots, void* stream);
 

@@ -59,6 +59,7 @@ struct ExtendArgs {
   int64_t ld;
   const int32_t* qo_indptr;
   const int32_t* prefix_lens;
+  const int32_t* order;     // optional: requests in the order their tiles are handed out
   int32_t B, hq, hkv, G;
   float scale_log2e;
   int64_t pool_slots;
@@ -68,17 +69,22 @@ struct ExtendArgs {
 };
 
 // Finds which request owns global tile index tg (tiles of BM rows, counted
-// request by request).  Wave-parallel prefix sum over the requests; the
-// result is uniform across the wave.  Returns false when tg is past the end.
+// request by request, in request order or in a.order's).  Wave-parallel
+// prefix sum over the requests; the result is uniform across the wave.
+// Returns false when tg is past the end.  An a.order entry outside [0, B)
+// owns no tiles.
 __device__ bool locate_tile(const ExtendArgs& a, int64_t tg, int& r, int& t) {
   const int lane = threadIdx.x & 63;
   int64_t acc = 0;
   for (int base = 0; base < a.B; base += 64) {
     const int i = base + lane;
-    int c = 0;
+    int c = 0, ri = i;
     if (i < a.B) {
-      const int64_t n = (int64_t)a.qo_indptr[i + 1] - a.qo_indptr[i];
-      c = (int)((n * a.G + BM - 1) / BM);
+      if (a.order) ri = a.order[i];
+      if ((unsigned)ri < (unsigned)a.B) {
+        const int64_t n = (int64_t)a.qo_indptr[ri + 1] - a.qo_indptr[ri];
+        c = (int)((n * a.G + BM - 1) / BM);
+      }
     }
     int s = c;
 #pragma unroll
@@ -92,7 +98,7 @@ __device__ bool locate_tile(const ExtendArgs& a, int64_t tg, int& r, int& t) {
       const int first = __ffsll((long long)mask) - 1;
       const int s_first = __shfl(s, first);
       const int c_first = __shfl(c, first);
-      r = base + first;
+      r = __shfl(ri, first);
       t = (int)(tg - (acc + s_first - c_first));
       return true;
     }
@@ -552,7 +558,8 @@ __global__ __launch_bounds__(256) void extend_f32(ExtendArgs a) {
 
 extern "C" int rkv_attn_extend(const void* q, const void* k_pool, const void* v_pool, void* o, float* lse,
                                const int32_t* req_to_token, int64_t ld, const int32_t* qo_indptr,
-                               const int32_t* prefix_lens, int32_t B, int64_t total_new,
+                               const int32_t* prefix_lens, const int32_t* req_order, int32_t B,
+                               int64_t total_new,
                                int32_t max_new, int32_t hq, int32_t hkv, int32_t d, float sm_scale,
                                int32_t dtype, int64_t pool_slots, void* stream) {
   rkv::clear_error();
@@ -570,6 +577,7 @@ extern "C" int rkv_attn_extend(const void* q, const void* k_pool, const void* v_
   ExtendArgs a;
   a.q = q; a.kp = k_pool; a.vp = v_pool; a.o = o; a.lse = lse;
   a.r2t = req_to_token; a.ld = ld; a.qo_indptr = qo_indptr; a.prefix_lens = prefix_lens;
+  a.order = req_order;
   a.B = B; a.hq = hq; a.hkv = hkv; a.G = hq / hkv;
   a.scale_log2e = sm_scale * 1.4426950408889634f;
   a.pool_slots = pool_slots;

@@ -102,7 +102,7 @@ def lib():
         "rkv_batch_append": (ctypes.c_int, [_vp, _i32, _vp, _i64, _vp, _vp]),
         "rkv_table_append": (ctypes.c_int, [_vp, _i64, _vp, _vp, _i32, _vp]),
         "rkv_kv_scatter": (ctypes.c_int, [_vp, _vp, _vp, _i64, _vp, _vp, _i64, _i32, _i32, _i32, _vp]),
-        "rkv_attn_extend": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _i32, _i64, _i32,
+        "rkv_attn_extend": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _i32, _i64, _i32,
                                            _i32, _i32, _i32, _f32, _i32, _i64, _vp]),
         "rkv_attn_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
         "rkv_attn_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32, _i32, _i32, _i32,
@@ -406,17 +406,21 @@ def table_append(req_to_token, seq_lens, new_slots, stream=None):
 
 
 def attn_extend(q, k_pool, v_pool, o, req_to_token, qo_indptr, prefix_lens, max_new, lse=None,
-                sm_scale=None, stream=None):
+                sm_scale=None, stream=None, order=None):
     """Causal extend attention of q [T, Hq, D] over each request's cached
-    prefix plus its new tokens; writes o (and lse when given)."""
-    _need_cuda(q, k_pool, v_pool, o, req_to_token, qo_indptr, prefix_lens, lse)
+    prefix plus its new tokens; writes o (and lse when given).  order: an
+    optional int32 device permutation of the requests, the order in which
+    their work is handed out (schedule only, e.g. longest first)."""
+    _need_cuda(q, k_pool, v_pool, o, req_to_token, qo_indptr, prefix_lens, lse, order)
     T, hq, d = q.shape
     P, hkv, _ = k_pool.shape
     B = int(prefix_lens.shape[0])
+    if order is not None and (order.dtype != prefix_lens.dtype or int(order.shape[0]) != B):
+        raise RkvError(EINVAL, "attn_extend: order must be int32 [B]")
     scale = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
     return _check(lib().rkv_attn_extend(
         _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(o), _ptr(lse), _ptr(req_to_token),
-        int(req_to_token.shape[1]), _ptr(qo_indptr), _ptr(prefix_lens), B, int(T), int(max_new),
+        int(req_to_token.shape[1]), _ptr(qo_indptr), _ptr(prefix_lens), _ptr(order), B, int(T), int(max_new),
         int(hq), int(hkv), int(d), scale, _dtype_code(q), int(P), _stream(stream)))
 
 
