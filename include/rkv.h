@@ -51,10 +51,11 @@ enum { RKV_F32 = 0, RKV_BF16 = 1 };
 typedef struct rkv_tree rkv_tree;
 
 /* Message for the last failing call on this thread ("" if none).  The pointer
- * stays valid until the next rkv_* call on the same thread. */
+ * stays valid until the next rkv_* call on the same thread.  (Library
+ * plumbing; it implements no passage of the pages.) */
 const char* rkv_last_error(void);
 
-/* Library version string, e.g. "rkv 0.1 gfx950". */
+/* Library version string, e.g. "rkv 0.1 gfx950".  (Library plumbing.) */
 const char* rkv_version(void);
 
 /* ------------------------------------------------------------------------
@@ -66,16 +67,29 @@ const char* rkv_version(void);
  *   children keyed by first label token, last_access (tick), lock (count).
  *   A global tick is incremented once at the start of every match and every
  *   insert, and of nothing else.  The allocator is a FIFO of slot ids.
+ *
+ * Slot ownership.  Every slot is at any time in exactly one place: free (in
+ * the FIFO), held by the caller (popped by rkv_alloc, rkv_batch_prepare or
+ * rkv_batch_append and not yet inserted or freed), or in the tree.  The
+ * library tracks this per slot (one byte each).  rkv_radix_insert,
+ * rkv_batch_commit and rkv_free accept only slots the caller holds, or, for
+ * an insert, the tree's own slot at its own position; anything else, or a
+ * caller slot given twice, is RKV_EINVAL with nothing changed.
  * ------------------------------------------------------------------------ */
 
 /* Creates a tree with an empty cache over a pool of `pool_slots` slots
- * (1 <= pool_slots <= 2^31-1).  `initial_free`, if not NULL, gives the
+ * (1 <= pool_slots <= 2^31-1): the walkthrough's starting point, an empty
+ * radix tree (unite.ai, "SGLang: Efficient Execution of Structured Language
+ * Model Programs", section "SGLang: Modelo de programacion y metodologia",
+ * Step 1), over a KV memory of fixed size whose limit later
+ * forces eviction (Step 5).  `initial_free`, if not NULL, gives the
  * initial FIFO order and must be a permutation of [0, pool_slots) (EINVAL
  * otherwise); NULL means 0, 1, ..., pool_slots-1.  *out receives the handle,
  * owned by the caller until rkv_tree_destroy. */
 int rkv_tree_create(rkv_tree** out, int64_t pool_slots, const int32_t* initial_free);
 
-/* Frees the tree and everything it owns.  NULL is a no-op. */
+/* Frees the tree and everything it owns (the counterpart of
+ * rkv_tree_create).  NULL is a no-op. */
 void rkv_tree_destroy(rkv_tree* t);
 
 /* Longest cached prefix of tok[0..n) (the page's "matching", Step 3 of the
@@ -118,57 +132,89 @@ int rkv_schedule(const rkv_tree* t, int32_t Q, const int32_t* tok, const int64_t
  * then treats them like tokens.  EINVAL on negative sizes or NULL buffers. */
 int rkv_image_keys(const uint8_t* bytes, int64_t len, int64_t n_tokens, int32_t* keys, uint64_t* out_hash);
 
-/* lock: +1 on the lock count of `node` and every ancestor up to, not
+/* The pages evict only nodes that the request being served does not need
+ * (unite.ai, "SGLang: Efficient Execution of Structured Language Model
+ * Programs", section "SGLang: Modelo de programacion y metodologia", Steps 5,
+ * 8 and 9: the continuing session's path survives, the least
+ * recently used other nodes go); they do not say how.  Reading taken: a
+ * reference count per node on the matched path of every request in flight.
+ * lock: +1 on the lock count of `node` and every ancestor up to, not
  * including, the root; locked nodes are never evicted.  unlock: -1 on the
  * same nodes; EINVAL (and no change) if any count would go negative or the
  * node does not exist.  Node 0 (the root) is a no-op for both. */
 int rkv_radix_lock(rkv_tree* t, int64_t node);
 int rkv_radix_unlock(rkv_tree* t, int64_t node);
 
-/* Inserts tok[0..n) with the caller's slots[0..n) (walkthrough Steps 2-3: a
+/* Inserts tok[0..n) with the caller's slots[0..n) (unite.ai, "SGLang:
+ * Efficient Execution of Structured Language Model Programs", section "SGLang:
+ * Modelo de programacion y metodologia", Steps 2-3: a
  * finished sequence enters the tree; the uncached rest becomes a new node).
  * Walks and splits as match does.  The tree takes ownership of all n slots:
  * for the m positions already cached the tree keeps its own slots and
  * appends each caller slot that differs from the tree's to the FIFO tail, in
  * increasing position; if m < n the rest becomes a new leaf (fresh id) under
  * the stop node.  Every node on the path, the new leaf included, gets
- * last_access = tick.  *out_cached = m.  Slots must be in [0, pool_slots). */
+ * last_access = tick.  *out_cached = m.  Slots must be in [0, pool_slots),
+ * and each must be the tree's own slot for its position or a slot the
+ * caller holds, given once (see Slot ownership above); otherwise RKV_EINVAL
+ * and nothing changes, checked by a read-only walk before the insert. */
 int rkv_radix_insert(rkv_tree* t, const int32_t* tok, const int32_t* slots, int64_t n,
                      int64_t* out_cached);
 
-/* LRU eviction (walkthrough Steps 5, 8, 9: whole nodes, least recently used
- * first, under a memory limit).  While fewer than `want` tokens are freed:
- * pick the unlocked non-root leaf with the smallest (last_access, id), append
+/* LRU eviction (unite.ai, "SGLang: Efficient Execution of Structured Language
+ * Model Programs", section "SGLang: Modelo de programacion y metodologia",
+ * Steps 5, 8, 9: whole nodes, least recently
+ * used first, under a memory limit; the RadixAttention bullet of section
+ * "Introduccion a SGLang" names eviction as one of the tree's operations).
+ * While fewer than `want` tokens are freed: pick the unlocked non-root leaf
+ * with the smallest (last_access, id), append
  * its slots to the FIFO tail in label order, detach it.  Whole leaves only,
  * so *out_freed may exceed want.  Returns RKV_EBUSY if no candidate is left
  * before `want` is reached; what was freed stays freed. */
 int rkv_radix_evict(rkv_tree* t, int64_t want, int64_t* out_freed);
 
-/* Pops n slots from the FIFO head into out[0..n).  RKV_ENOSPC, with no
+/* Slot allocation: the walkthrough closes by noting that RadixAttention
+ * allocates and evicts nodes dynamically as requests arrive (unite.ai,
+ * "SGLang: Efficient Execution of Structured Language Model Programs", section
+ * "SGLang: Modelo de programacion y metodologia", the paragraph after
+ * Step 9); the pages do not say how KV memory is handed out.  Reading taken:
+ * one pool of token slots with a FIFO free list.
+ * Pops n slots from the FIFO head into out[0..n).  RKV_ENOSPC, with no
  * change, if fewer than n are free (no implicit eviction).  The caller owns
  * the slots until it passes them to rkv_radix_insert or rkv_free. */
 int rkv_alloc(rkv_tree* t, int64_t n, int32_t* out);
 
-/* Appends slots[0..n) to the FIFO tail in the given order.  EINVAL if a
- * slot is out of range or the FIFO would exceed pool_slots entries. */
+/* Appends slots[0..n) to the FIFO tail in the given order (the
+ * counterpart of rkv_alloc).  EINVAL, with no change, if a slot is out of
+ * range, not held by the caller, or given twice. */
 int rkv_free(rkv_tree* t, const int32_t* slots, int64_t n);
 
 /* out[8] = {cached tokens, free slots, evictable tokens (in nodes with lock
  * 0), locked tokens, nodes (non-root), matched tokens over all prepared
  * requests, prompt tokens over all prepared requests, evicted tokens}.
- * Cache hit rate = out[5] / out[6]. */
+ * Cache hit rate = out[5] / out[6], the quantity the article reports
+ * without a formula (unite.ai, "SGLang: Efficient Execution of Structured
+ * Language Model Programs", section "SGLang: Evaluacion y resultados": hit
+ * rates of 50-99 %; section "Despliegue en produccion"). */
 int rkv_stats(rkv_tree* t, int64_t out[8]);
 
-/* Canonical dump: DFS from the root, children in ascending first-token
+/* Canonical dump, for tests that compare two trees bit for bit (no passage:
+ * inspection only): DFS from the root, children in ascending first-token
  * order; per node the int64 values (id, parent id (-1 for the root),
  * last_access, lock, len, label[len], slots[len]).  Writes at most cap
  * values; *len receives the full length (call with cap 0 to size). */
 int rkv_radix_serialize(rkv_tree* t, int64_t* buf, int64_t cap, int64_t* len);
 
-/* FIFO contents head to tail; same sizing convention as serialize. */
+/* FIFO contents head to tail; same sizing convention as serialize
+ * (inspection only, like serialize). */
 int rkv_free_list(rkv_tree* t, int32_t* buf, int64_t cap, int64_t* len);
 
-/* Prepares one batch of B requests whose token ids are
+/* The serving step before attention (unite.ai, "SGLang: Efficient Execution of
+ * Structured Language Model Programs", section "SGLang: Modelo de programacion
+ * y metodologia": Step 3, a new prompt finds its
+ * cached prefix and reuses its KV; Step 7, a batch of requests sharing
+ * few-shot examples; Steps 5, 8 and 9, nodes evicted to make room).
+ * Prepares one batch of B requests whose token ids are
  * tok[tok_indptr[r] .. tok_indptr[r+1]) (lengths L_r >= 1, L_r <= ld).
  * For r = 0..B-1 in order: match the first L_r - 1 tokens (so every request
  * computes at least its last token), lock the stop node.  Then with
@@ -187,8 +233,18 @@ int rkv_batch_prepare(rkv_tree* t, int32_t B, const int32_t* tok, const int64_t*
                       int32_t* seq_lens, int32_t* qo_indptr, int32_t* new_slots,
                       int64_t new_cap, int64_t* out_nodes);
 
-/* Commits a prepared batch: for r = 0..B-1, insert the full sequence with
- * slots req_to_token[r, 0..L_r), then unlock nodes[r]. */
+/* The serving step after attention (unite.ai, "SGLang: Efficient Execution of
+ * Structured Language Model Programs", section "SGLang: Modelo de programacion
+ * y metodologia", Steps 2, 3 and 7: the finished
+ * sequences enter the tree, new parts as new nodes, shared parts split off).
+ * Commits a prepared batch: for r = 0..B-1, insert the full sequence with
+ * slots req_to_token[r, 0..L_r), then unlock nodes[r].  Every argument is
+ * checked before the first insert, so RKV_EINVAL changes nothing: lengths
+ * in [1, ld], slots in range, nodes that exist, lock counts that cover
+ * every unlock the batch makes on each node (a node named by k requests
+ * needs a count >= k), and slots as rkv_radix_insert requires them, with no
+ * caller slot in two requests.  The sequences must be the ones the table
+ * rows describe: after rkv_batch_append, the grown sequences. */
 int rkv_batch_commit(rkv_tree* t, int32_t B, const int32_t* tok, const int64_t* tok_indptr,
                      const int32_t* req_to_token, int64_t ld, const int64_t* nodes);
 
@@ -227,7 +283,12 @@ int rkv_batch_append(rkv_tree* t, int32_t B, int32_t* req_to_token, int64_t ld, 
  * stream synchronization.
  * ------------------------------------------------------------------------ */
 
-/* k_pool[slots[i]] = k_new[i] and v_pool[slots[i]] = v_new[i] for
+/* Writes the new tokens' K/V into their pool slots, where later requests
+ * that share the prefix read them instead of recomputing them (unite.ai,
+ * "SGLang: Efficient Execution of Structured Language Model Programs", section
+ * "Introduccion a SGLang", RadixAttention bullet: a request's KV
+ * cache is kept after processing so other calls can reuse it).
+ * k_pool[slots[i]] = k_new[i] and v_pool[slots[i]] = v_new[i] for
  * i in [0, T); k_new, v_new are [T, Hkv, D].  A plain copy: bit-exact, every
  * other pool row untouched.  Slots must be distinct (duplicates race).  T = 0
  * is a no-op. */
@@ -244,7 +305,14 @@ int rkv_kv_scatter(const void* k_new, const void* v_new, const int32_t* slots, i
 int rkv_table_append(int32_t* req_to_token, int64_t ld, int32_t* seq_lens, const int32_t* new_slots,
                      int32_t B, void* stream);
 
-/* Extend (prefill over a cached prefix).  Request r has p_r = prefix_lens[r]
+/* Extend (prefill over a cached prefix): the attention of a prompt whose
+ * prefix was found in the tree; only its new tokens are computed, and they
+ * attend to the reused cached KV plus their own (unite.ai, "SGLang: Efficient
+ * Execution of Structured Language Model Programs", section "SGLang: Modelo de
+ * programacion y metodologia", Step 3; the
+ * extend primitive in that section's list adds text to a prompt).  The
+ * attention itself is plain causal softmax attention; the pages give no
+ * formula for it.  Request r has p_r = prefix_lens[r]
  * cached tokens and n_r = qo_indptr[r+1] - qo_indptr[r] new ones, whose
  * queries are q rows qo_indptr[r] .. qo_indptr[r+1].  New row j sits at
  * position c = p_r + j and attends causally to keys 0..c of its own request:
@@ -254,8 +322,9 @@ int rkv_table_append(int32_t* req_to_token, int64_t ld, int32_t* seq_lens, const
  *   `lse` may be NULL).
  * total_new must equal qo_indptr[B] (the number of q rows) and max_new must
  * be >= every n_r; together they size the grid (a smaller max_new leaves rows
- * of the longer requests unwritten).  The new tokens' K/V must already be in the pool (rkv_kv_scatter).
- * bf16: QK^T and PV on bf16 MFMA with fp32 accumulation, fp32 online
+ * of the longer requests unwritten).  The new tokens' K/V must already be in
+ * the pool (rkv_kv_scatter). bf16: QK^T and PV on bf16 MFMA with fp32
+ * accumulation, fp32 online
  * softmax, softmax weights rounded to bf16 for PV, o rounded to bf16 (RNE).
  * The row sums that normalize o (and give lse) are sums of those same
  * rounded weights, so bf16 lse is within ln(1 + 2^-8) of the exact value.
@@ -276,11 +345,18 @@ int rkv_attn_extend(const void* q, const void* k_pool, const void* v_pool, void*
                     int64_t pool_slots, void* stream);
 
 /* Bytes of device workspace rkv_attn_decode needs for these sizes
- * (num_splits as passed to rkv_attn_decode).  0 on bad arguments. */
+ * (num_splits as passed to rkv_attn_decode); sizing for the call below.
+ * 0 on bad arguments. */
 size_t rkv_attn_decode_workspace_bytes(int32_t B, int32_t hq, int32_t d, int32_t max_seq_len,
                                        int32_t num_splits);
 
-/* Single-token decode: q, o are [B, Hq, D]; request r's query is its last
+/* Single-token decode: the attention step of generation, one new token
+ * per request (unite.ai, "SGLang: Efficient Execution of Structured Language
+ * Model Programs", section "SGLang: Modelo de programacion y metodologia", the
+ * gen primitive; section "Introduccion a
+ * SGLang" notes that decoding proceeds one token at a time), reading every
+ * key of the request's context through its table, cached prefix included.
+ * q, o are [B, Hq, D]; request r's query is its last
  * position L_r - 1 (L_r = seq_lens[r] >= 1, its own K/V already scattered)
  * and attends to all L_r keys req_to_token[r, 0..L_r) (same formula as
  * extend).  Split-KV: the keys of a request are cut into S_r contiguous
@@ -341,7 +417,8 @@ int rkv_cascade_plan(const int32_t* req_to_token, int64_t ld, const int32_t* seq
                      int64_t jobs_cap, int64_t* out_n_jobs, int32_t* out_tail_splits);
 
 /* Bytes of device workspace rkv_attn_decode_cascade needs: n_records
- * records of Hq rows of (d + 4) fp32.  0 on bad arguments. */
+ * records of Hq rows of (d + 4) fp32 (sizing for the call below).  0 on bad
+ * arguments. */
 size_t rkv_attn_decode_cascade_workspace_bytes(int64_t n_records, int32_t hq, int32_t d);
 
 /* Decode (same inputs, outputs and formula as rkv_attn_decode) following a
@@ -352,8 +429,9 @@ size_t rkv_attn_decode_cascade_workspace_bytes(int64_t n_records, int32_t hq, in
  * per (kv head, job): the job's keys are gathered once, from the row of
  * request perm[first], for the count * (Hq/Hkv) query columns of its
  * members (bf16 MFMA; max_members * Hq/Hkv columns at most 32 for d = 128
- * and 64 for d = 64, ENOTSUP otherwise), and one wave or workgroup per (request, tail split)
- * covers the private keys; phase 2 merges each request's records.  bf16
+ * and 64 for d = 64, ENOTSUP otherwise), and one wave or workgroup per
+ * (request, tail split) covers the private keys; phase 2 merges each request's
+ * records.  bf16
  * only (ENOTSUP otherwise); arithmetic as in rkv_attn_decode's MFMA path.
  * The plan's values are checked in the kernels before they index anything:
  * a job or request that does not fit is skipped, and with RKV_DEBUG=1 the

@@ -17,7 +17,11 @@
 //     by binary search; sorted order is also the canonical dump order;
 //   - LRU candidates: an ordered set of (last_access, id) holding exactly the
 //     non-root leaves with lock 0, so eviction pops its minimum;
-//   - FIFO: a ring buffer of pool_slots int32 entries.
+//   - FIFO: a ring buffer of pool_slots int32 entries;
+//   - owner: one byte per slot (free, held by the caller, in the tree), so
+//     insert, commit and free can reject a slot the caller does not hold
+//     before they change anything (a foreign slot pushed to the FIFO would
+//     otherwise overrun the ring or hand one slot out twice).
 
 #include <algorithm>
 #include <cstdint>
@@ -63,6 +67,11 @@ struct rkv_tree {
   // FIFO ring
   std::vector<int32_t> ring;
   int64_t head = 0, count = 0;
+  // who holds each slot; kPending marks a caller slot already seen while a
+  // call checks its arguments (a repeat is then caught) and is undone before
+  // the call returns
+  enum : uint8_t { kFree = 0, kCaller = 1, kTree = 2, kPending = 3 };
+  std::vector<uint8_t> owner;
   // tree
   Node root;
   std::unordered_map<int64_t, std::unique_ptr<Node>> nodes;  // non-root nodes by id
@@ -79,6 +88,7 @@ struct rkv_tree {
     int64_t i = head + count;
     if (i >= pool) i -= pool;
     ring[i] = s;
+    owner[(size_t)s] = kFree;
     ++count;
   }
   // pops n slots (n <= count) in FIFO order into each of the non-null
@@ -86,6 +96,7 @@ struct rkv_tree {
   void pop_n(int64_t n, int32_t* out_a, int32_t* out_b) {
     while (n > 0) {
       const int64_t run = std::min<int64_t>(n, pool - head);
+      for (int64_t i = 0; i < run; ++i) owner[(size_t)ring[(size_t)(head + i)]] = kCaller;
       if (out_a) std::memcpy(out_a, ring.data() + head, sizeof(int32_t) * (size_t)run);
       if (out_b) std::memcpy(out_b, ring.data() + head, sizeof(int32_t) * (size_t)run);
       if (out_a) out_a += run;
@@ -212,6 +223,51 @@ struct rkv_tree {
     return m;
   }
 
+  // peek that also copies the cached slots of the matched positions
+  int64_t peek_slots(const int32_t* tok, int64_t n, int32_t* slots) const {
+    const Node* node = &root;
+    int64_t m = 0;
+    while (m < n) {
+      auto it = std::lower_bound(node->kids.begin(), node->kids.end(), tok[m],
+                                 [](const std::pair<int32_t, Node*>& a, int32_t b) { return a.first < b; });
+      if (it == node->kids.end() || it->first != tok[m]) break;
+      const Node* c = it->second;
+      const int64_t lab = (int64_t)c->label.size();
+      const int64_t lim = std::min<int64_t>(lab, n - m);
+      const int64_t k = common_from(c->label.data(), tok + m, 1, lim);
+      std::memcpy(slots + m, c->slots.data(), sizeof(int32_t) * (size_t)k);
+      m += k;
+      if (k < lab) break;
+      node = c;
+    }
+    return m;
+  }
+
+  // Argument check of an insert of tok[0..n) with slots sl[0..n), read-only
+  // on the tree: every position either holds the tree's own slot for it or a
+  // slot the caller holds, and no caller slot appears twice (across all the
+  // calls made before the matching unmark_pending()).  Such an insert only
+  // pushes caller slots, each once, so the FIFO never exceeds the pool.  The
+  // same holds when earlier inserts of one batch grow the matched part: the
+  // extra positions then hold caller slots that are pushed.
+  bool owned_ok(const int32_t* tok, const int32_t* sl, int64_t n) {
+    tmp_slots.resize((size_t)std::max<int64_t>(n, 1));
+    const int64_t m = peek_slots(tok, n, tmp_slots.data());
+    for (int64_t i = 0; i < n; ++i) {
+      if (i < m && sl[i] == tmp_slots[(size_t)i]) continue;
+      uint8_t& o = owner[(size_t)sl[i]];
+      if (o != kCaller) return false;
+      o = kPending;
+      pending.push_back(sl[i]);
+    }
+    return true;
+  }
+  void unmark_pending() {
+    for (int32_t s : pending) owner[(size_t)s] = kCaller;
+    pending.clear();
+  }
+  std::vector<int32_t> pending;
+
   int64_t do_match(const int32_t* tok, int64_t n, int32_t* slots, int64_t* node_id) {
     ++tick;
     int64_t m = 0;
@@ -248,6 +304,7 @@ struct rkv_tree {
       Node* leaf = make_node();
       leaf->label.assign(tok + m, tok + n);
       leaf->slots.assign(sl + m, sl + n);
+      for (int64_t i = m; i < n; ++i) owner[(size_t)sl[i]] = kTree;
       leaf->parent = stop;
       leaf->last_access = tick;
       add_kid(stop, leaf);
@@ -315,6 +372,7 @@ int rkv_tree_create(rkv_tree** out, int64_t pool_slots, const int32_t* initial_f
   try {
     t->pool = pool_slots;
     t->ring.resize((size_t)pool_slots);
+    t->owner.assign((size_t)pool_slots, rkv_tree::kFree);
     if (initial_free) {
       std::vector<uint8_t> seen((size_t)pool_slots, 0);
       for (int64_t i = 0; i < pool_slots; ++i) {
@@ -401,6 +459,9 @@ int rkv_radix_insert(rkv_tree* t, const int32_t* tok, const int32_t* slots, int6
     return bad("rkv_radix_insert: bad argument");
   for (int64_t i = 0; i < n; ++i)
     if (!slot_ok(t, slots[i])) return bad("rkv_radix_insert: slot out of range");
+  const bool ok = t->owned_ok(tok, slots, n);
+  t->unmark_pending();
+  if (!ok) return bad("rkv_radix_insert: a slot is neither the tree's own for its position nor held by the caller, or it repeats");
   *out_cached = t->do_insert(tok, slots, n);
   return RKV_OK;
 }
@@ -427,6 +488,17 @@ int rkv_free(rkv_tree* t, const int32_t* slots, int64_t n) {
   if (t->count + n > t->pool) return bad("rkv_free: more slots than the pool holds");
   for (int64_t i = 0; i < n; ++i)
     if (!slot_ok(t, slots[i])) return bad("rkv_free: slot out of range");
+  bool held = true;
+  for (int64_t i = 0; i < n && held; ++i) {
+    uint8_t& o = t->owner[(size_t)slots[i]];
+    if (o != rkv_tree::kCaller) held = false;
+    else {
+      o = rkv_tree::kPending;
+      t->pending.push_back(slots[i]);
+    }
+  }
+  t->unmark_pending();
+  if (!held) return bad("rkv_free: a slot is not held by the caller, or it repeats");
   for (int64_t i = 0; i < n; ++i) t->push(slots[i]);
   return RKV_OK;
 }
@@ -530,21 +602,35 @@ int rkv_batch_commit(rkv_tree* t, int32_t B, const int32_t* tok, const int64_t* 
   if (B == 0) return RKV_OK;
   if (!tok || !tok_indptr || !req_to_token || !nodes || ld < 1)
     return bad("rkv_batch_commit: bad argument");
+  // every check comes before the first insert, so EINVAL changes nothing
+  std::unordered_map<Node*, int64_t> unlocks;   // node -> unlocks this batch makes on it
   for (int32_t r = 0; r < B; ++r) {
     const int64_t L = tok_indptr[r + 1] - tok_indptr[r];
-    if (L < 1 || L > ld) return bad("rkv_batch_commit: every length must be in [1, ld]");
+    if (tok_indptr[r] < 0 || L < 1 || L > ld) return bad("rkv_batch_commit: every length must be in [1, ld]");
     const int32_t* row = req_to_token + (int64_t)r * ld;
     for (int64_t i = 0; i < L; ++i)
       if (!slot_ok(t, row[i])) return bad("rkv_batch_commit: slot out of range");
-    if (!t->find(nodes[r])) return bad("rkv_batch_commit: no such node");
+    Node* n = t->find(nodes[r]);
+    if (!n) return bad("rkv_batch_commit: no such node");
+    for (Node* p = n; p != &t->root; p = p->parent) ++unlocks[p];
   }
+  // a split during the inserts gives the new upper node the lower one's
+  // lock count, which covers the unlocks still to come through it
+  for (const auto& kv : unlocks)
+    if (kv.first->lock < kv.second) return bad("rkv_batch_commit: node is not locked");
+  bool ok = true;
+  for (int32_t r = 0; r < B && ok; ++r) {
+    const int64_t L = tok_indptr[r + 1] - tok_indptr[r];
+    ok = t->owned_ok(tok + tok_indptr[r], req_to_token + (int64_t)r * ld, L);
+  }
+  t->unmark_pending();
+  if (!ok)
+    return bad("rkv_batch_commit: a slot is neither the tree's own for its position nor held by the caller, "
+               "or it repeats within the batch");
   for (int32_t r = 0; r < B; ++r) {
     const int64_t L = tok_indptr[r + 1] - tok_indptr[r];
     t->do_insert(tok + tok_indptr[r], req_to_token + (int64_t)r * ld, L);
-    Node* n = t->find(nodes[r]);
-    for (Node* p = n; p != &t->root; p = p->parent)
-      if (p->lock <= 0) return bad("rkv_batch_commit: node is not locked");
-    t->lock_path(n, -1);
+    t->lock_path(t->find(nodes[r]), -1);
   }
   return RKV_OK;
 }

@@ -112,9 +112,17 @@ class RadixKVCache:
 
     def commit(self, batch: Batch, seqs=None):
         """Inserts the batch's sequences (`seqs` when the batch was extended
-        by append) and unlocks their paths."""
-        self.tree.batch_commit(batch.seqs if seqs is None else seqs, batch.host["req_to_token"],
-                               batch.host["nodes"])
+        by append) and unlocks their paths.  Every sequence must be as long
+        as its table row (seq_lens, grown by append): the tree inserts only
+        len(seq) entries of a row, so a shorter sequence would leave the
+        slots after it neither cached nor free."""
+        seqs = batch.seqs if seqs is None else seqs
+        lens = seqs.lens if isinstance(seqs, rkv.TokenBatch) else np.array([len(s) for s in seqs])
+        want = batch.host["seq_lens"]
+        if len(lens) != len(want) or not np.array_equal(np.asarray(lens, dtype=np.int64), want.astype(np.int64)):
+            raise ValueError("commit: each sequence must be as long as its table row (after append, "
+                             "pass the grown sequences)")
+        self.tree.batch_commit(seqs, batch.host["req_to_token"], batch.host["nodes"])
 
     # ---------------------------------------------------------------- device
     def store(self, batch: Batch, k_new, v_new, stream=None):

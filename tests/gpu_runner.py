@@ -21,12 +21,18 @@ from oracle.pool import OraclePool, scatter as oscatter
 from oracle.radix import OracleTree
 
 TOL = {"f32": 1e-5, "bf16": 2e-2}
-# bf16 extend, and bf16 decode with >= 4 query heads per kv head (both on
-# matrix cores), sum the same bf16-rounded weights that PV uses, so their lse
-# carries that rounding: |ln(sum p^) - ln(sum p)| <= ln(1 + 2^-8) < 3.9e-3
-# (unit roundoff of bf16).  fp32 paths and the vector-unit decode keep fp32
-# weights.
-LSE_TOL = {"f32": 1e-5, "bf16": 3.9e-3}
+# lse bounds.  fp32 paths, and the vector-unit decode, keep fp32 softmax
+# weights: 1e-5 / 1e-4.  bf16 extend, and bf16 decode with >= 4 query heads
+# per kv head (both on matrix cores), normalize by the sum of the same
+# bf16-rounded weights that PV multiplies.  Each weight then carries a
+# relative error of at most u = 2^-8 (bf16 unit roundoff, round to nearest
+# even), so the sum lies in [l(1 - u), l(1 + u)] and its log within
+# -ln(1 - 2^-8) = 3.9139e-3 of ln l.  The fp32 part adds at most
+# n * 2^-24 relative for the sum of n weights (6.9e-5 at 1152 keys; far
+# less in practice, which the 120k-key tests show) plus |lse| * 2^-23 for
+# forming m + log2(l) in fp32: 1e-4 covers both at the benchmark sizes.
+LSE_BF16_ROUNDING = -math.log1p(-2.0 ** -8)
+LSE_TOL = {"f32": 1e-5, "bf16": LSE_BF16_ROUNDING + 1e-4}
 
 
 def log(msg):

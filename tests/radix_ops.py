@@ -202,5 +202,10 @@ def drive(trees, seed, n_ops, pool, vocab, max_len):
         check_structure(nodes)
         owned = [s for nd in nodes for s in nd["slots"]]
         assert sorted(owned + trees[0].free_list() + held_slots) == list(range(pool))
-        same([list(t.stats()) for t in trees])
+        st = same([list(t.stats()) for t in trees])
+        # the first five stats are sums over the dump and the free list
+        non_root = [nd for nd in nodes if nd["id"] != 0]
+        assert st[:5] == [sum(len(nd["label"]) for nd in non_root), len(trees[0].free_list()),
+                          sum(len(nd["label"]) for nd in non_root if nd["lock"] == 0),
+                          sum(len(nd["label"]) for nd in non_root if nd["lock"] > 0), len(non_root)], st
     return counts
