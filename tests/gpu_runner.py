@@ -65,12 +65,19 @@ def needed_slots(shape, phases, select):
     return need
 
 
+ORACLE_CHUNK = 8   # requests per oracle call, each followed by a progress line
+
+
 def run(shape, phases, select=lambda i, B: None, num_splits=0, content_device="cuda",
-        with_lse=True, sparse=False, cascade=None):
+        with_lse=True, sparse=False, cascade=None, phase_source=None):
     """Returns a list of per-checked-phase dicts with GPU and oracle outputs
     restricted to the selected requests' rows.  cascade: None for plain
     decode, else a dict of cascade_plan arguments for prefix-shared decode
-    (the native plan is then asserted equal to the oracle's)."""
+    (the native plan is then asserted equal to the oracle's).
+    phase_source: instead of a fixed `phases` list, a callable
+    (cache, oracle_tree) -> iterator of phases, advanced after each phase is
+    committed on both trees (a serving loop that decides the next batch
+    from the cache's state); not with sparse=True."""
     from prefix_shared_kv_host_amd.engine import RadixKVCache
 
     dt = content.torch_dtype(shape.dtype)
@@ -80,10 +87,12 @@ def run(shape, phases, select=lambda i, B: None, num_splits=0, content_device="c
     cache = RadixKVCache(shape.pool, shape.hkv, shape.d, dt, "cuda", perm)
     keep = None
     if sparse:
+        assert phase_source is None, "a sparse oracle pool needs the phases up front"
         keep = np.zeros(shape.pool, dtype=bool)
         keep[list(needed_slots(shape, phases, select))] = True
     out = []
-    for i, ph in enumerate(phases):
+    source = phases if phase_source is None else phase_source(cache, otree)
+    for i, ph in enumerate(source):
         t0 = time.time()
         st, otb = otree.batch_prepare(ph.seqs)
         assert st == 0
@@ -122,8 +131,17 @@ def run(shape, phases, select=lambda i, B: None, num_splits=0, content_device="c
             rq = list(range(B)) if reqs is None else list(reqs)
             qn = q.float().cpu().numpy()
             if ph.kind == "extend":
-                o_ref, lse_ref = oatt.extend(qn, opool, otb["req_to_token"], otb["qo_indptr"],
-                                             otb["prefix_lens"], shape.hq, shape.hkv, requests=rq)
+                o_ref = np.full((rows, shape.hq, shape.d), np.nan)
+                lse_ref = np.full((rows, shape.hq), np.nan)
+                for c in range(0, len(rq), ORACLE_CHUNK):
+                    part = rq[c:c + ORACLE_CHUNK]
+                    t1 = time.time()
+                    o_p, l_p = oatt.extend(qn, opool, otb["req_to_token"], otb["qo_indptr"],
+                                           otb["prefix_lens"], shape.hq, shape.hkv, requests=part)
+                    pr = np.concatenate([np.arange(otb["qo_indptr"][r], otb["qo_indptr"][r + 1]) for r in part])
+                    o_ref[pr], lse_ref[pr] = o_p[pr], l_p[pr]
+                    if len(rq) > ORACLE_CHUNK:
+                        log(f"  oracle: requests {c}..{c + len(part) - 1} of {len(rq)} ({time.time() - t1:.1f}s)")
                 row_idx = np.concatenate([np.arange(otb["qo_indptr"][r], otb["qo_indptr"][r + 1]) for r in rq])
             else:
                 o_ref, lse_ref = oatt.decode(qn, opool, otb["req_to_token"], otb["seq_lens"],

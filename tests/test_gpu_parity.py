@@ -77,50 +77,121 @@ def test_extend_c2_every_row(name):
         assert np.abs(res[0]["o_ref"]).max() > 0.5      # peaked weights: |o| ~ 1
 
 
-@pytest.mark.timeout(400)
-def test_extend_c4_subset():
+@pytest.mark.timeout(900)
+def test_extend_c4_every_request():
+    """Every row of the 64/8-head extend half: 64 requests x 256 new tokens x
+    64 heads, contexts 2304-8192, in the launch configuration the engine and
+    the benchmark use (its work order included)."""
     shape, phases = configs.c4()
-    sel = lambda i, B: ([0, 5, 17, 22, 31, 40, 53, 63] if phases[i].kind == "extend" else [])
+    sel = lambda i, B: (None if phases[i].kind == "extend" else [])
     res, _ = G.run(shape, phases[:3], select=sel, sparse=True)
+    assert [len(r["requests"]) for r in res] == [64]
     G.check(res, "bf16", "c4-extend")
 
 
-def chat_selector(name, per_batch, seed=5):
-    """c5 / c5e: a seeded sample of `per_batch` turns of every batch, plus
-    every turn whose cached history was (partly) evicted and is recomputed.
-    Returns (shape, phases, selector, recompute_turns)."""
+def tenth(seed, i, B):
+    """A seeded tenth (rounded up) of a batch's B turns."""
+    rng = np.random.default_rng(seed * 1000 + i)
+    return set(rng.choice(B, size=min(B, -(-B // 10)), replace=False).tolist())
+
+
+def recompute_turns(step_tags, tables, seqlen):
+    """Turns of a batch whose cached history lost tokens to eviction: turn
+    t > 0 reuses less than the whole of its turn t - 1."""
+    return [r for r, (sid, t) in enumerate(step_tags)
+            if t > 0 and tables["prefix_lens"][r] < seqlen[(sid, t - 1)]]
+
+
+def chat_selector(name, seed=5):
+    """c5 / c5e: a seeded tenth of the turns of every batch, plus every turn
+    whose cached history was (partly) evicted and is recomputed.
+    Returns (shape, phases, selector, recompute_turns, sampled_count)."""
     shape, phases = configs.build(name)
     batches, tags = configs.chat_trace(shape.seed)
     assert len(batches) == len(phases)
     seqlen = {st: len(seq) for b, tg in zip(batches, tags) for seq, st in zip(b, tg)}
-    recompute = []
+    recompute, sampled = [], []
 
     def sel(i, B, tables):
-        rng = np.random.default_rng(seed * 1000 + i)
-        pick = set(rng.choice(B, size=min(per_batch, B), replace=False).tolist())
-        for r, (sid, t) in enumerate(tags[i]):
-            if t > 0 and tables["prefix_lens"][r] < seqlen[(sid, t - 1)]:
-                pick.add(r)
-                recompute.append((i, r))
-        return sorted(pick)
-    return shape, phases, sel, recompute
+        pick = tenth(seed, i, B)
+        sampled.append(len(pick))
+        again = recompute_turns(tags[i], tables, seqlen)
+        recompute.extend((i, r) for r in again)
+        return sorted(pick | set(again))
+    return shape, phases, sel, recompute, sampled
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name,per_batch", [("c5", 3), ("c5e", 2)])
-def test_extend_c5_chat(name, per_batch):
+@pytest.mark.parametrize("name", ["c5", "c5e"])
+def test_extend_c5_chat(name):
     """Multi-turn chat through the whole cache: 89 batches of prepare, store,
-    extend and commit; c5e evicts under a 2^19-slot pool and recomputes."""
-    shape, phases, sel, recompute = chat_selector(name, per_batch)
+    extend and commit; c5e evicts under a 2^19-slot pool and recomputes.  A
+    tenth of every batch's turns is compared, and every recompute turn."""
+    shape, phases, sel, recompute, sampled = chat_selector(name)
     res, _ = G.run(shape, phases, select=sel, sparse=True)
     G.check(res, "bf16", name)
-    G.log(f"{name}: {sum(len(r['requests']) for r in res)} turns checked, "
+    n_turns = sum(len(ph.seqs) for ph in phases)
+    checked = sum(len(r["requests"]) for r in res)
+    # the selector runs twice (slot dry run + the run itself)
+    G.log(f"{name}: {checked} of {n_turns} turns checked ({100 * checked / n_turns:.1f} %), "
           f"{len(recompute) // 2} of them recompute evicted history")
+    assert sum(sampled) // 2 * 10 >= n_turns
     if name == "c5e":
-        # the selector runs twice (slot dry run + the run itself)
         assert len(recompute) // 2 == 32
     else:
         assert not recompute
+
+
+@pytest.mark.timeout(900)
+def test_cache_aware_serving_c5e():
+    """Cache-aware scheduling on the GPU (the article's section "SGLang:
+    Evaluacion y resultados" credits it with hit rates near the optimum):
+    the chat trace under the 2^19-slot pool, served as a queue in which a
+    session's next turn is runnable once its previous turn ran.  At every
+    step the cache's native tree ranks the runnable turns (rkv_schedule,
+    longest reusable prefix first) and the oracle tree ranks them too (equal
+    order and matched lengths asserted); the first 64 run as one batch
+    through prepare, store, extend and commit, with the tables asserted
+    bit-exact against the oracle tree's.  A tenth of every batch and every
+    turn that recomputes evicted history is compared with the oracle's
+    attention; the reuse equals the host-only queue replay's."""
+    from prefix_shared_kv_host_amd import rkv, serving
+    shape, _ = configs.build("c5e")
+    batches, tags = configs.chat_trace(shape.seed)
+    turns = {st: seq for b, tg in zip(batches, tags) for seq, st in zip(b, tg)}
+    arrival = [st for tg in tags for st in tg]
+    seqlen = {st: len(seq) for st, seq in turns.items()}
+    step_tags, recompute = [], []
+
+    def source(cache, otree):
+        finished, pending = set(), list(arrival)
+        while pending:
+            ready = [st for st in pending if st[1] == 0 or (st[0], st[1] - 1) in finished]
+            seqs = [turns[st] for st in ready]
+            order_n, matched_n = cache.tree.schedule(seqs)
+            order_o, matched_o = otree.schedule(seqs)
+            assert order_n.tolist() == list(order_o) and matched_n.tolist() == list(matched_o)
+            pick = [ready[int(i)] for i in order_n[:64]]
+            step_tags.append(pick)
+            yield configs.Phase("extend", [turns[st] for st in pick])
+            finished.update(pick)
+            taken = set(pick)
+            pending = [st for st in pending if st not in taken]
+
+    def sel(i, B, tables):
+        again = recompute_turns(step_tags[i], tables, seqlen)
+        recompute.extend(again)
+        return sorted(tenth(7, i, B) | set(again))
+
+    res, cache = G.run(shape, None, select=sel, phase_source=source)
+    G.check(res, "bf16", "c5e cache-aware")
+    reused = [int(x) for r in res for x in r["batch"].host["prefix_lens"]]
+    ref = serving.run_queue(rkv.Tree(shape.pool, configs.free_list(shape.pool, shape.seed)), turns, arrival,
+                            "cache")
+    assert [st for tg in step_tags for st in tg] == ref["order"] and reused == ref["reused"]
+    assert len(step_tags) == ref["steps"]
+    G.log(f"cache-aware c5e: {len(step_tags)} steps, hit rate {ref['hit_rate']:.4f}, "
+          f"{len(recompute)} recompute turns, {sum(len(r['requests']) for r in res)} turns checked")
 
 
 # ---------------------------------------------------------------- decode
