@@ -376,6 +376,26 @@ int rkv_attn_decode(const void* q, const void* k_pool, const void* v_pool, void*
                     float sm_scale, int32_t dtype, int32_t num_splits, void* workspace,
                     size_t ws_bytes, int64_t pool_slots, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * decode as rkv_attn_decode (same arguments minus the workspace, same
+ * kernels, bit-identical results), with the split partials in a scratch
+ * array that the library holds, one per GPU it runs on, for the life of the
+ * process: 32 MiB (33554432 bytes).  A call whose
+ * rkv_attn_decode_workspace_bytes(B, hq, d, max_seq_len, num_splits) exceeds
+ * that returns RKV_EINVAL and launches nothing.  The call allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine); its first call on a
+ * device takes the array's device address (hipGetSymbolAddress).  Every call
+ * on one GPU shares that GPU's array: calls that overlap on one GPU (two
+ * streams, or two host threads) race and must be ordered by the caller.
+ * Under RKV_DEBUG=1 out-of-range slots are reported through a flag held the
+ * same way. */
+int rkv_attn_decode_noalloc(const void* q, const void* k_pool, const void* v_pool, void* o, float* lse,
+                            const int32_t* req_to_token, int64_t ld, const int32_t* seq_lens,
+                            int32_t B, int32_t max_seq_len, int32_t hq, int32_t hkv, int32_t d,
+                            float sm_scale, int32_t dtype, int32_t num_splits, int64_t pool_slots,
+                            void* stream);
+
 /* ------------------------------------------------------------------------
  * Prefix-shared ("cascade") decode.  Requests under one radix node gather the
  * same slots for that node's keys (the page's RadixAttention bullet, section

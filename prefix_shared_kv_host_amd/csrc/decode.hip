@@ -27,6 +27,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <string>
 #include <type_traits>
 
@@ -957,27 +958,15 @@ extern "C" size_t rkv_attn_decode_workspace_bytes(int32_t B, int32_t hq, int32_t
   return (size_t)B * hq * S * (d + 4) * sizeof(float);
 }
 
-extern "C" int rkv_attn_decode(const void* q, const void* k_pool, const void* v_pool, void* o, float* lse,
-                               const int32_t* req_to_token, int64_t ld, const int32_t* seq_lens,
-                               int32_t B, int32_t max_seq_len, int32_t hq, int32_t hkv, int32_t d,
-                               float sm_scale, int32_t dtype, int32_t num_splits, void* workspace,
-                               size_t ws_bytes, int64_t pool_slots, void* stream) {
-  rkv::clear_error();
-  if (B < 0 || hq < 1 || hkv < 1 || max_seq_len < 1 || ld < max_seq_len || pool_slots < 1 ||
-      num_splits < 0 || !(sm_scale > 0.f))
-    return rkv::fail(RKV_EINVAL, "rkv_attn_decode: bad sizes");
-  if (dtype != RKV_F32 && dtype != RKV_BF16) return rkv::fail(RKV_ENOTSUP, "rkv_attn_decode: dtype");
-  if (d != 64 && d != 128) return rkv::fail(RKV_ENOTSUP, "rkv_attn_decode: head_dim must be 64 or 128");
-  if (hq % hkv != 0 || hq / hkv > 16) return rkv::fail(RKV_ENOTSUP, "rkv_attn_decode: Hq/Hkv must be an integer <= 16");
-  if (B == 0) return RKV_OK;
-  if (!q || !k_pool || !v_pool || !o || !req_to_token || !seq_lens)
-    return rkv::fail(RKV_EINVAL, "rkv_attn_decode: NULL pointer");
-  const uintptr_t al = (uintptr_t)q | (uintptr_t)k_pool | (uintptr_t)v_pool | (uintptr_t)o;
-  if (al & 15) return rkv::fail(RKV_EINVAL, "rkv_attn_decode: tensors must be 16-byte aligned");
-  const size_t need = rkv_attn_decode_workspace_bytes(B, hq, d, max_seq_len, num_splits);
+namespace {
+
+// Plain split-KV decode for both entry points: `workspace` holds the split
+// partials, `flag` (nullable) the debug error flag.
+int decode_launch(const char* who, const void* q, const void* k_pool, const void* v_pool, void* o, float* lse,
+                  const int32_t* req_to_token, int64_t ld, const int32_t* seq_lens, int32_t B,
+                  int32_t max_seq_len, int32_t hq, int32_t hkv, int32_t d, float sm_scale, int32_t dtype,
+                  int32_t num_splits, void* workspace, int64_t pool_slots, int* flag, hipStream_t st) {
   const int64_t S = splits_extent(max_seq_len, num_splits);
-  if (S > 1 && (!workspace || ws_bytes < need || ((uintptr_t)workspace & 15)))
-    return rkv::fail(RKV_EINVAL, "rkv_attn_decode: workspace missing or too small");
   DecodeArgs a;
   a.q = q; a.kp = k_pool; a.vp = v_pool; a.o = o; a.lse = lse;
   a.r2t = req_to_token; a.ld = ld; a.seq_lens = seq_lens;
@@ -994,17 +983,120 @@ extern "C" int rkv_attn_decode(const void* q, const void* k_pool, const void* v_
   a.tail_begin = nullptr;
   a.n_records = 0;
   a.tail_chunk = 0;
-  if (int rc = rkv::debug_flag(&a.err)) return rc;
+  a.err = flag;
   int64_t grid = (int64_t)S * B * ((hkv + a.hb - 1) / a.hb) * a.hg;
   grid = (grid + rkv::kXcds - 1) / rkv::kXcds * rkv::kXcds;
-  if (grid > 0x7fffffff) return rkv::fail(RKV_ENOTSUP, "rkv_attn_decode: grid too large");
-  hipStream_t st = (hipStream_t)stream;
+  if (grid > 0x7fffffff) return rkv::fail(RKV_ENOTSUP, std::string(who) + ": grid too large");
   if (dtype == RKV_BF16) {
     if (d == 128) launch_all<uint16_t, 128>(a, grid, st); else launch_all<uint16_t, 64>(a, grid, st);
   } else {
     if (d == 128) launch_all<float, 128>(a, grid, st); else launch_all<float, 64>(a, grid, st);
   }
-  return rkv::finish_launch("rkv_attn_decode", st, a.err);
+  return rkv::finish_launch(who, st, a.err);
+}
+
+// Argument checks shared by both entry points (everything but the workspace).
+int decode_check(const char* who, const void* q, const void* k_pool, const void* v_pool, const void* o,
+                 const int32_t* req_to_token, int64_t ld, const int32_t* seq_lens, int32_t B,
+                 int32_t max_seq_len, int32_t hq, int32_t hkv, int32_t d, float sm_scale, int32_t dtype,
+                 int32_t num_splits, int64_t pool_slots) {
+  const std::string w(who);
+  if (B < 0 || hq < 1 || hkv < 1 || max_seq_len < 1 || ld < max_seq_len || pool_slots < 1 ||
+      num_splits < 0 || !(sm_scale > 0.f))
+    return rkv::fail(RKV_EINVAL, w + ": bad sizes");
+  if (dtype != RKV_F32 && dtype != RKV_BF16) return rkv::fail(RKV_ENOTSUP, w + ": dtype");
+  if (d != 64 && d != 128) return rkv::fail(RKV_ENOTSUP, w + ": head_dim must be 64 or 128");
+  if (hq % hkv != 0 || hq / hkv > 16) return rkv::fail(RKV_ENOTSUP, w + ": Hq/Hkv must be an integer <= 16");
+  if (B == 0) return RKV_OK;
+  if (!q || !k_pool || !v_pool || !o || !req_to_token || !seq_lens) return rkv::fail(RKV_EINVAL, w + ": NULL pointer");
+  const uintptr_t al = (uintptr_t)q | (uintptr_t)k_pool | (uintptr_t)v_pool | (uintptr_t)o;
+  if (al & 15) return rkv::fail(RKV_EINVAL, w + ": tensors must be 16-byte aligned");
+  return RKV_OK;
+}
+
+// ---- scratch of the decode entry point that allocates nothing
+// A file-scope device array, one per GPU the library runs on, held until the
+// process ends; its device address (and that of a debug flag beside it) is
+// taken once per device with hipGetSymbolAddress, with the device current,
+// and kept.  In host code `scratch` names a host-side stand-in, never the
+// device memory: only the kept pointers are passed to kernels.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+__device__ __align__(256) char scratch[kScratchBytes];
+__device__ int scratch_flag;
+
+struct ScratchPtrs {
+  void* ws = nullptr;
+  int* flag = nullptr;
+};
+std::mutex g_scratch_mu;
+ScratchPtrs g_scratch[64];
+
+int scratch_ptrs(ScratchPtrs* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+    return rkv::fail(RKV_EHIP, "rkv_attn_decode_noalloc: hipGetDevice failed");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  ScratchPtrs& s = g_scratch[dev];
+  if (!s.ws) {
+    void* ws = nullptr;
+    void* flag = nullptr;
+    if (hipGetSymbolAddress(&ws, HIP_SYMBOL(scratch)) != hipSuccess || !ws)
+      return rkv::fail(RKV_EHIP, "rkv_attn_decode_noalloc: hipGetSymbolAddress(scratch) failed");
+    if (hipGetSymbolAddress(&flag, HIP_SYMBOL(scratch_flag)) != hipSuccess || !flag)
+      return rkv::fail(RKV_EHIP, "rkv_attn_decode_noalloc: hipGetSymbolAddress(scratch_flag) failed");
+    s.ws = ws;
+    s.flag = (int*)flag;
+  }
+  *out = s;
+  return RKV_OK;
+}
+
+}  // namespace
+
+extern "C" int rkv_attn_decode(const void* q, const void* k_pool, const void* v_pool, void* o, float* lse,
+                               const int32_t* req_to_token, int64_t ld, const int32_t* seq_lens,
+                               int32_t B, int32_t max_seq_len, int32_t hq, int32_t hkv, int32_t d,
+                               float sm_scale, int32_t dtype, int32_t num_splits, void* workspace,
+                               size_t ws_bytes, int64_t pool_slots, void* stream) {
+  rkv::clear_error();
+  const char* who = "rkv_attn_decode";
+  if (int rc = decode_check(who, q, k_pool, v_pool, o, req_to_token, ld, seq_lens, B, max_seq_len, hq, hkv, d,
+                            sm_scale, dtype, num_splits, pool_slots))
+    return rc;
+  if (B == 0) return RKV_OK;
+  const size_t need = rkv_attn_decode_workspace_bytes(B, hq, d, max_seq_len, num_splits);
+  const int64_t S = splits_extent(max_seq_len, num_splits);
+  if (S > 1 && (!workspace || ws_bytes < need || ((uintptr_t)workspace & 15)))
+    return rkv::fail(RKV_EINVAL, "rkv_attn_decode: workspace missing or too small");
+  int* flag = nullptr;
+  if (int rc = rkv::debug_flag(&flag)) return rc;
+  return decode_launch(who, q, k_pool, v_pool, o, lse, req_to_token, ld, seq_lens, B, max_seq_len, hq, hkv, d,
+                       sm_scale, dtype, num_splits, workspace, pool_slots, flag, (hipStream_t)stream);
+}
+
+extern "C" int rkv_attn_decode_noalloc(const void* q, const void* k_pool, const void* v_pool, void* o, float* lse,
+                                       const int32_t* req_to_token, int64_t ld, const int32_t* seq_lens,
+                                       int32_t B, int32_t max_seq_len, int32_t hq, int32_t hkv, int32_t d,
+                                       float sm_scale, int32_t dtype, int32_t num_splits, int64_t pool_slots,
+                                       void* stream) {
+  rkv::clear_error();
+  const char* who = "rkv_attn_decode_noalloc";
+  if (int rc = decode_check(who, q, k_pool, v_pool, o, req_to_token, ld, seq_lens, B, max_seq_len, hq, hkv, d,
+                            sm_scale, dtype, num_splits, pool_slots))
+    return rc;
+  if (B == 0) return RKV_OK;
+  const size_t need = rkv_attn_decode_workspace_bytes(B, hq, d, max_seq_len, num_splits);
+  if (need > kScratchBytes)
+    return rkv::fail(RKV_EINVAL, "rkv_attn_decode_noalloc: these sizes need " + std::to_string(need) +
+                                     " bytes of split partials, more than the " + std::to_string(kScratchBytes) +
+                                     " this entry point holds; use rkv_attn_decode with a workspace");
+  ScratchPtrs sp;
+  if (int rc = scratch_ptrs(&sp)) return rc;
+  // the partials are written before they are read, so nothing needs clearing;
+  // the debug flag starts at zero and finish_launch clears it after a report
+  return decode_launch(who, q, k_pool, v_pool, o, lse, req_to_token, ld, seq_lens, B, max_seq_len, hq, hkv, d,
+                       sm_scale, dtype, num_splits, sp.ws, pool_slots, rkv::debug_mode() ? sp.flag : nullptr,
+                       (hipStream_t)stream);
 }
 
 extern "C" size_t rkv_attn_decode_cascade_workspace_bytes(int64_t n_records, int32_t hq, int32_t d) {

@@ -33,8 +33,11 @@ EXPORTS = (
     "rkv_attn_decode", "rkv_radix_peek", "rkv_schedule", "rkv_cascade_plan",
     "rkv_attn_decode_cascade_workspace_bytes", "rkv_attn_decode_cascade", "rkv_penalty_admit",
     "rkv_penalty_accumulate", "rkv_penalty_apply", "rkv_image_keys", "rkv_batch_append",
-    "rkv_table_append",
+    "rkv_table_append", "rkv_attn_decode_noalloc",
 )
+
+# the scratch that rkv_attn_decode_noalloc holds per GPU (include/rkv.h)
+DECODE_NOALLOC_MAX_BYTES = 32 << 20
 
 
 class TokenBatch:
@@ -107,6 +110,8 @@ def lib():
         "rkv_attn_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
         "rkv_attn_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32, _i32, _i32, _i32,
                                            _i32, _f32, _i32, _i32, _vp, _sz, _i64, _vp]),
+        "rkv_attn_decode_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32, _i32, _i32,
+                                                   _i32, _i32, _f32, _i32, _i32, _i64, _vp]),
         "rkv_cascade_plan": (ctypes.c_int, [c_i32p, _i64, c_i32p, _i32, _i32, _i32, _i32, _i32, c_i32p,
                                             c_i32p, c_i32p, c_i32p, _i64, c_i64p, c_i32p]),
         "rkv_attn_decode_cascade_workspace_bytes": (_sz, [_i64, _i32, _i32]),
@@ -442,6 +447,21 @@ def attn_decode(q, k_pool, v_pool, o, req_to_token, seq_lens, max_seq_len, works
         int(req_to_token.shape[1]), _ptr(seq_lens), int(B), int(max_seq_len), int(hq), int(hkv),
         int(d), scale, _dtype_code(q), int(num_splits), _ptr(workspace), int(ws_bytes), int(P),
         _stream(stream)))
+
+
+def attn_decode_noalloc(q, k_pool, v_pool, o, req_to_token, seq_lens, max_seq_len, lse=None, num_splits=0,
+                        sm_scale=None, stream=None):
+    """attn_decode without a workspace argument: the split partials go to the
+    scratch the library holds per GPU (rkv_attn_decode_noalloc; it allocates
+    nothing, and calls that overlap on one GPU race)."""
+    _need_cuda(q, k_pool, v_pool, o, req_to_token, seq_lens, lse)
+    B, hq, d = q.shape
+    P, hkv, _ = k_pool.shape
+    scale = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
+    return _check(lib().rkv_attn_decode_noalloc(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(o), _ptr(lse), _ptr(req_to_token),
+        int(req_to_token.shape[1]), _ptr(seq_lens), int(B), int(max_seq_len), int(hq), int(hkv),
+        int(d), scale, _dtype_code(q), int(num_splits), int(P), _stream(stream)))
 
 
 class CascadePlan:
