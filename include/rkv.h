@@ -277,10 +277,12 @@ int rkv_batch_append(rkv_tree* t, int32_t B, int32_t* req_to_token, int64_t ld, 
  * contiguous elements); q and o are [rows, Hq, D]; req_to_token is int32
  * [B, ld] row-major.  dtype is RKV_F32 or RKV_BF16 for q, pools and o alike.
  * Supported: D in {64, 128}, Hq % Hkv == 0, Hq / Hkv <= 16; anything else is
- * RKV_ENOTSUP.  Gathered slots are range-checked in the kernels: an entry
- * outside [0, pool_slots) reads as zeros (scatter skips it) and, with the
- * environment variable RKV_DEBUG=1, makes the call return RKV_EINVAL after a
- * stream synchronization.
+ * RKV_ENOTSUP.  No kernel reads or writes outside the pool whatever the
+ * tables hold: a gathered entry outside [0, pool_slots) reads as zeros in
+ * the decode kernels and the f32 extend, is clamped to slot pool_slots - 1 in
+ * the bf16 extend (the output of such a row is meaningless either way), and
+ * is skipped by scatter.  With the environment variable RKV_DEBUG=1 such an
+ * entry makes the call return RKV_EINVAL after a stream synchronization.
  * ------------------------------------------------------------------------ */
 
 /* Writes the new tokens' K/V into their pool slots, where later requests
@@ -327,7 +329,8 @@ int rkv_table_append(int32_t* req_to_token, int64_t ld, int32_t* seq_lens, const
  * accumulation, fp32 online
  * softmax, softmax weights rounded to bf16 for PV, o rounded to bf16 (RNE).
  * The row sums that normalize o (and give lse) are sums of those same
- * rounded weights, so bf16 lse is within ln(1 + 2^-8) of the exact value.
+ * rounded weights: each is within a factor 1 +- 2^-8 of its exact value, so
+ * bf16 lse is within -ln(1 - 2^-8) (plus fp32 rounding) of the exact value.
  * f32: fp32 arithmetic throughout.  B = 0 or total_new = 0 is a no-op.
  * req_order (nullable, int32 [B], device): a permutation of the requests in
  * which the bf16 path hands out work (each request's row tiles still in

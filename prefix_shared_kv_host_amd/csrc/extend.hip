@@ -13,14 +13,24 @@
 //     heads share every K/V tile they read.  Work items are ordered kv-head
 //     major and dealt to XCDs in contiguous ranges (requests sharing a prefix
 //     read the same rows of one head from one L2).
-//   * 4 waves x 32 rows, two workgroups per CU.  Each wave keeps its Q (two
-//     16-row blocks) in registers for the whole key loop.
+//   * 4 waves x 32 rows per workgroup, two workgroups per CU: two waves per
+//     SIMD, each keeping its Q (two 16-row blocks) in registers.  Within a
+//     wave the key loop is software pipelined by hand, so that a stall of one
+//     wave does not have to be covered by the other: the softmax runs on
+//     32-key half tiles, and each half tile is one block of fenced stages in
+//     which the QK MFMAs of the next half tile sit beside the exponentials of
+//     this one, and its PV MFMAs beside the row maxima of the next.
 //   * K/V tiles of 64 keys go global -> LDS by 16-byte LDS DMA
-//     (global_load_lds), one slot lookup per row: K two tiles ahead, V one,
-//     each in two stages; the slot indices reach LDS by 4-byte DMA straight
-//     from the table.  The gathers of a tile are spread over the next tile's
-//     QK steps.  K is read as 16-byte rows (ds_read_b128); V stays row-major
+//     (global_load_lds), one slot lookup per row.  The K tiles are shifted
+//     half a tile against V (K tile t holds keys 64t-32 .. 64t+31), so QK
+//     runs one half tile ahead of PV while an iteration still consumes one K
+//     and one V tile.  K runs two tiles ahead, V one; the slot indices reach
+//     LDS by 4-byte DMA straight from the table, one more tile ahead.  The
+//     gathers of a tile are spread over the QK stages of the iteration
+//     before.  K is read as 16-byte rows (ds_read_b128); V stays row-major
 //     and the V^T operand comes from transposed reads (ds_read_b64_tr_b16).
+//     Gathered slots are clamped into the pool; a separate check kernel,
+//     launched only in debug mode, reports table entries outside it.
 //   * S^T = K Q^T, so a lane owns one query: its row max / row sum are lane
 //     values plus cross-lane swaps.  K rows are placed in LDS in an order
 //     that makes the S^T accumulator of a lane hold 8 consecutive keys, which
@@ -28,7 +38,7 @@
 //     never leave registers.
 //   * fp32 online softmax in the log2 domain (exp2 with log2(e) folded into
 //     the scale); weights rounded to bf16 for PV; o rounded to bf16 (RNE).
-//   * causal masking only on tiles that reach past a wave's first query.
+//   * causal masking only on tiles that reach past a workgroup's first query.
 // fp32 path: one wave per (query row, head), fp32 FMA throughout.
 
 #include <hip/hip_runtime.h>
@@ -48,6 +58,9 @@ using rkv::f32x4;
 
 constexpr int BM = 128;   // query rows per workgroup
 constexpr int BN = 64;    // keys per tile
+constexpr int NWAVES = 4; // waves per workgroup
+constexpr int QB = 2;     // 16-row query blocks per wave (32 rows)
+static_assert(NWAVES * QB * 16 == BM, "waves x rows cover the workgroup's rows");
 
 struct ExtendArgs {
   const void* q;
@@ -133,13 +146,30 @@ __device__ __forceinline__ int swz_v(int row) {
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 #define RKV_LDS __attribute__((address_space(3)))
 
-// Global -> LDS copies: lane l's 16 (4) bytes land at lds_base + 16*l (4*l).
+// Global -> LDS copies (gfx950 LDS DMA): lane l's 16 (4) bytes land at
+// lds_base + 16*l (4*l).  Issued as inline assembly: the compiler counts a
+// global_load_lds it emits itself as an LDS access that may complete out of
+// order, and then waits for every LDS operation (lgkmcnt(0)) wherever it
+// needs any one of them, so each operand read fetched ahead would be drained
+// together with the one it waits for.  From assembly the copy is invisible
+// to that bookkeeping; it writes LDS only (no register), and every stage it
+// fills is read only after a full s_waitcnt and a barrier.  Every LDS DMA
+// of this file's kernels goes through these two, so no compiler-generated
+// code there keeps a value in M0 across them (the compiler warns that a
+// clobbered M0 is reserved; nothing of its own relies on M0 here).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const void* g, const void* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (RKV_LDS void*)lds_base, 16, 0, 0);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(RKV_LDS void*)lds_base))
+               : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void* g, const void* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (RKV_LDS void*)lds_base, 4, 0, 0);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+               :: "v"(g), "s"(__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(RKV_LDS void*)lds_base))
+               : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // Softmax weights are kept relative to a per-row reference maximum that is
 // only raised when a tile's maximum exceeds it by more than 2^8 (log2 units):
@@ -148,27 +178,28 @@ __device__ __forceinline__ void dma4(const void* g, const void* lds_base) {
 constexpr float kRescaleThreshold = 8.0f;
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void extend_bf16(ExtendArgs a) {
+__global__ __launch_bounds__(NWAVES * 64, 2) void extend_bf16(ExtendArgs a) {
   constexpr int ROWB = D * 2;              // bytes of one (slot, kv head) row
   constexpr int CH = D / 8;                // 16-byte chunks per row
   constexpr int KSTEPS = D / 32;           // QK contraction steps
   constexpr int DBLK = D / 16;             // PV output blocks
   constexpr int RPI = 1024 / ROWB;         // rows one wave moves per DMA instruction
-  constexpr int NDMA = BN / (RPI * 4);     // DMA instructions per wave per tile (each of K, V)
+  constexpr int NDMA = BN / (RPI * NWAVES);  // DMA instructions per wave per tile (each of K, V)
+  constexpr int GPH = NDMA / 2;            // of those, issued in each half-tile QK phase
   constexpr int TILEB = BN * ROWB;         // bytes of one K or V tile
+  static_assert(GPH * 2 == NDMA && GPH >= 1, "the gathers of a tile split over its two QK phases");
 
-  // K runs one tile ahead of V (QK of tile t+1 overlaps the softmax and PV
-  // of tile t), each in two stages; slot indices run one more tile ahead.
-  // The stages are separate LDS objects addressed with a compile-time parity
-  // (the key loop is unrolled by two), so the compiler can tell that the
-  // operand reads of one stage never alias the DMA still writing the other
-  // and does not wait for that DMA before them.
+  // K runs one tile ahead of V, each in two stages; slot indices run one
+  // more tile ahead.  The stages are separate LDS objects addressed with a
+  // compile-time parity (the key loop is unrolled by two), so the compiler
+  // can tell that the operand reads of one stage never alias the DMA still
+  // writing the other and does not wait for that DMA before them.
   __shared__ __attribute__((aligned(16))) char K0[TILEB];
   __shared__ __attribute__((aligned(16))) char K1[TILEB];
   __shared__ __attribute__((aligned(16))) char V0[TILEB];
   __shared__ __attribute__((aligned(16))) char V1[TILEB];
   // slot indices of four tiles, stored in the order the gather lanes use
-  // them (each lane's NDMA slots of a tile are contiguous: one LDS read)
+  // them (each lane's NDMA slots of a tile are contiguous)
   __shared__ __attribute__((aligned(16))) int32_t SlK[4][BN];
   __shared__ __attribute__((aligned(16))) int32_t SlV[4][BN];
   auto kbuf = [&](auto par) -> char* {
@@ -206,19 +237,20 @@ __global__ __launch_bounds__(256, 2) void extend_bf16(ExtendArgs a) {
   const int first_mask_tile = min(ntiles, (p + row0 / G) / BN);
 
   // ---- queries of this wave: rows row0 + wave*32 + qb*16 + l16
-  bf16x8 qreg[2][KSTEPS];
-  int qlim[2], qhead[2], qtok[2];
-  bool qvalid[2];
+  bf16x8 qreg[QB][KSTEPS];
+  int qlim[QB], qhead[QB], qtok[QB];
+  bool qvalid[QB];
   const uint16_t* qbase = (const uint16_t*)a.q;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int row = row0 + wave * 32 + qb * 16 + l16;
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = row0 + wave * (QB * 16) + qb * 16 + l16;
     qvalid[qb] = row < rows_total && (int64_t)q0 + row / G < a.total_new && p + row / G < kv_end;
     const int j = qvalid[qb] ? row / G : 0;
     const int hh = qvalid[qb] ? row % G : 0;
     qtok[qb] = q0 + j;
     qhead[qb] = g * G + hh;
-    // last visible key, relative to the first key this lane holds in a tile
+    // last visible key, relative to the first key this lane holds in a
+    // 32-key half tile
     qlim[qb] = (qvalid[qb] ? p + j : kv_end - 1) - 8 * gq;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
@@ -229,16 +261,20 @@ __global__ __launch_bounds__(256, 2) void extend_bf16(ExtendArgs a) {
     }
   }
 
-  f32x4 oacc[2][DBLK];
+  f32x4 oacc[QB][DBLK];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) oacc[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float mref[2] = {-INFINITY, -INFINITY};
+  float mref[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) mref[qb] = -INFINITY;
   // row sums of the bf16 weights, accumulated on the MFMA (all-ones A
   // operand) so that numerator and denominator use the same rounded weights;
   // every element of lacc[qb] holds the lane's full row sum
-  f32x4 lacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  f32x4 lacc[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) lacc[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
   const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
   const float c = a.scale_log2e;
 
@@ -248,7 +284,6 @@ __global__ __launch_bounds__(256, 2) void extend_bf16(ExtendArgs a) {
   const int32_t* row_tab = a.r2t + (int64_t)r * a.ld;
   const uint32_t P = (uint32_t)min(a.pool_slots, (int64_t)0x7fffffff);
   const uint32_t slot_bytes = (uint32_t)a.hkv * ROWB;
-  bool bad = false;   // some gathered slot was outside the pool
   // DMA lane roles: row (within the wave's run of RPI rows) and LDS chunk
   const int drow = lane / CH;
   const int dch = lane % CH;
@@ -261,218 +296,301 @@ __global__ __launch_bounds__(256, 2) void extend_bf16(ExtendArgs a) {
   const int key_v = pos_row(lane);
   const char* kg = (const char*)a.kp + (uint64_t)g * ROWB;
   const char* vg = (const char*)a.vp + (uint64_t)g * ROWB;
-  // gathers of one tile; slots outside [0, pool_slots) are replaced by 0 and
-  // reported through the return value
-  auto gather = [&](const int32_t* slots, char* dst, const char* src, auto is_k) -> bool {
-    int32_t sv[NDMA];
-    const int32_t* mine = slots + (wave * RPI + drow) * NDMA;
-    if constexpr (NDMA == 4) {
-      const int4 v = *(const int4*)mine;
-      sv[0] = v.x; sv[1] = v.y; sv[2] = v.z; sv[3] = v.w;
-    } else {
-#pragma unroll
-      for (int j = 0; j < NDMA; ++j) sv[j] = mine[j];
-    }
-    bool bad = false;
-#pragma unroll
-    for (int j = 0; j < NDMA; ++j) {
-      const bool ok = (uint32_t)sv[j] < P;
-      bad |= !ok;
-      const uint32_t slot = ok ? (uint32_t)sv[j] : 0u;
-      const int R = dma_row(wave, j, drow);
-      const int lch = dch ^ (decltype(is_k)::value ? swz_k<CH>(R) : swz_v<CH>(R));
-      dma16(src + (uint64_t)slot * slot_bytes + lch * 16, dst + (wave * NDMA + j) * 1024);
-    }
-    return bad;
-  };
-  auto dma_k = [&](int tile, auto par) { return gather(SlK[tile & 3], kbuf(par), kg, std::true_type{}); };
-  auto dma_v = [&](int tile, auto par) { return gather(SlV[tile & 3], vbuf(par), vg, std::false_type{}); };
-  // gather instruction j alone (slot read from LDS just before it), so the
-  // gathers of a tile can be spread over the MFMA work instead of queueing
-  // behind one another at the start of an iteration
-  auto gather1 = [&](const int32_t* slots, char* dst, const char* src, int j, auto is_k) -> bool {
-    const int32_t sv = slots[(wave * RPI + drow) * NDMA + j];
-    const bool ok = (uint32_t)sv < P;
-    const uint32_t slot = ok ? (uint32_t)sv : 0u;
+  // gather instruction j of a tile (slot read from LDS just before it), so
+  // the gathers of a tile can be spread over the MFMA work instead of
+  // queueing behind one another at the start of an iteration; a slot
+  // outside [0, pool_slots) is clamped to the pool's last slot
+  auto gather1 = [&](const int32_t* slots, char* dst, const char* src, int j, auto is_k) {
+    const uint32_t slot = min((uint32_t)slots[(wave * RPI + drow) * NDMA + j], P - 1);
     const int R = dma_row(wave, j, drow);
     const int lch = dch ^ (decltype(is_k)::value ? swz_k<CH>(R) : swz_v<CH>(R));
     dma16(src + (uint64_t)slot * slot_bytes + lch * 16, dst + (wave * NDMA + j) * 1024);
-    return !ok;
   };
-  // slot indices of tile `tile` into stage tile & 3 (waves 0 and 1, one
-  // 4-byte DMA each, straight from the table; clamped keys past the end)
+  auto dma_k = [&](int tile, auto par) {
+#pragma unroll
+    for (int j = 0; j < NDMA; ++j) gather1(SlK[tile & 3], kbuf(par), kg, j, std::true_type{});
+  };
+  auto dma_v = [&](int tile, auto par) {
+#pragma unroll
+    for (int j = 0; j < NDMA; ++j) gather1(SlV[tile & 3], vbuf(par), vg, j, std::false_type{});
+  };
+  // slot indices of tile `tile` into stage tile & 3 (wave 0 for K, wave 1
+  // for V, one 4-byte DMA each, straight from the table; keys clamped into
+  // [0, kv_end)).  K tile k holds keys [64k - 32, 64k + 32): shifted half a
+  // tile against V, so that QK runs one half tile ahead of PV while each
+  // iteration still reads one K tile and one V tile.
   auto dma_slots = [&](int tile) {
-    if (wave == 0) dma4(row_tab + min(tile * BN + key_k, kv_end - 1), SlK[tile & 3]);
+    if (wave == 0) dma4(row_tab + min(max(tile * BN - BN / 2 + key_k, 0), kv_end - 1), SlK[tile & 3]);
     else if (wave == 1) dma4(row_tab + min(tile * BN + key_v, kv_end - 1), SlV[tile & 3]);
   };
 
-  // ---- S^T = K Q^T for one tile (both query blocks)
-  // With gathers on, contraction step s is followed by gather instruction s
-  // of K(gk) (into the stage of parity gpar) and of V(gk - 1) (the other
-  // stage); KSTEPS == NDMA for 64-key tiles.
-  static_assert(KSTEPS == NDMA, "one K and one V gather per contraction step");
-  auto qk = [&](auto par, f32x4 (&sacc)[2][4], auto gather_tag, int gk) {
-    constexpr bool GATHER = decltype(gather_tag)::value;
-    using GPAR = std::integral_constant<int, 1 - decltype(par)::value>;
-    const char* ks = kbuf(par);
+  // The softmax runs on 32-key halves of a tile ("half tiles", numbered u =
+  // 2*tile + h), so that QK of half tile u+1 overlaps the exponentials of u
+  // and PV of u overlaps the row maxima of u+1, with the scores of just two
+  // half tiles live: s_ev / s_od hold the even / odd half tiles, and
+  // s[qb][kk] holds, for lane group gq, the keys 8*gq + 4*kk + [0..3] of the
+  // half tile for its query (K rows are placed in LDS so).
+
+  // raw row maxima of the latest half tile, and the raise thresholds
+  float mt[QB], thr[QB];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < QB; ++qb) thr[qb] = -INFINITY;
+  // the rare rescale: raise the reference of every row of the wave that
+  // needs it and rescale its O and row sum (PV of the previous half tile
+  // has been issued)
+  auto rescale = [&](const float (&mtv)[QB]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) sacc[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int qb = 0; qb < QB; ++qb) {
+      const float mn = fmaxf(mref[qb], mtv[qb] * c);
+      const float alpha = __builtin_amdgcn_exp2f(mref[qb] - mn);
+      mref[qb] = mn;
+      thr[qb] = (mn + kRescaleThreshold) / c;
+      lacc[qb] *= alpha;
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const int row = kb * 16 + l16;
-        const bf16x8 ka = __builtin_bit_cast(
-            bf16x8, *(const uint4*)(ks + row * ROWB + (((s * 4 + gq) ^ swz_k<CH>(row)) << 4)));
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          sacc[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qreg[qb][s], sacc[qb][kb], 0, 0, 0);
-      }
-      if constexpr (GATHER) {
-        bad |= gather1(SlK[gk & 3], kbuf(GPAR{}), kg, s, std::true_type{});
-        bad |= gather1(SlV[(gk - 1) & 3], vbuf(par), vg, s, std::false_type{});
-      }
+      for (int db = 0; db < DBLK; ++db) oacc[qb][db] *= alpha;
     }
   };
 
-  // ---- softmax of tile `tile` (scores in sacc) and O^T += V^T P^T; the QK
-  //      of the next tile is issued in the same basic block so its MFMAs
-  //      overlap this tile's exponentials
-  // scores of the tile being finished and of the next one; the two buffers
-  // swap roles with the tile parity, so no copy is needed between tiles
-  f32x4 s_even[2][4], s_odd[2][4];
-  auto step = [&](int tile, auto par, auto mask_tag, auto next_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    constexpr bool NEXT = decltype(next_tag)::value;
-    using NPAR = std::integral_constant<int, 1 - decltype(par)::value>;
-    constexpr bool EVEN = decltype(par)::value == 0;
-    f32x4 (&s_cur)[2][4] = EVEN ? s_even : s_odd;
-    f32x4 (&s_nxt)[2][4] = EVEN ? s_odd : s_even;
-    float mt[2];
+  // ---- operands and softmax pieces of one half tile
+  // K operand i = (contraction step i/2, 16-key block i%2) of half h of the
+  // K tile in ks
+  auto k_op = [&](const char* ks, int h, int i) __attribute__((always_inline)) -> bf16x8 {
+    const int row = (2 * h + (i & 1)) * 16 + l16;
+    return __builtin_bit_cast(bf16x8, *(const uint4*)(ks + row * ROWB + ((((i >> 1) * 4 + gq) ^ swz_k<CH>(row)) << 4)));
+  };
+  // V^T operand of output block db, half h of the V tile in vs: two
+  // transposed reads of 4 keys each.  Lane p of group gq points at key row
+  // 32*h + 8*gq + 4*hh + p/4, d = 16*db + 4*(p%4); lane i then receives
+  // keys [0..3] of that row run at d = 16*db + i.
+  auto v_op = [&](const char* vs, int h, int db) __attribute__((always_inline)) -> bf16x8 {
+    v4i16 part[2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      if constexpr (MASK) {
-        const int lim = qlim[qb] - tile * BN;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (32 * (kb >> 1) + 4 * (kb & 1) + i > lim) s_cur[qb][kb][i] = -INFINITY;
-      }
-      float mx = fmaxf(fmaxf(s_cur[qb][0][0], s_cur[qb][0][1]), fmaxf(s_cur[qb][0][2], s_cur[qb][0][3]));
-#pragma unroll
-      for (int kb = 1; kb < 4; ++kb)
-        mx = fmaxf(mx, fmaxf(fmaxf(s_cur[qb][kb][0], s_cur[qb][kb][1]), fmaxf(s_cur[qb][kb][2], s_cur[qb][kb][3])));
-      mx = rkv::max_xor16(mx);
-      mx = rkv::max_xor32(mx);
-      mt[qb] = mx * c;
+    for (int hh = 0; hh < 2; ++hh) {
+      const int row = h * 32 + gq * 8 + hh * 4 + (l16 >> 2);
+      const int d = db * 16 + 4 * (l16 & 3);
+      const char* ptr = vs + row * ROWB + ((((d >> 3) ^ swz_v<CH>(row))) << 4) + ((d & 7) << 1);
+      part[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((RKV_LDS v4i16*)ptr);
     }
-    if (__builtin_amdgcn_ballot_w64(mt[0] > mref[0] + kRescaleThreshold ||
-                                    mt[1] > mref[1] + kRescaleThreshold)) {
+    return __builtin_bit_cast(
+        bf16x8, make_uint4(__builtin_bit_cast(uint2, part[0]).x, __builtin_bit_cast(uint2, part[0]).y,
+                           __builtin_bit_cast(uint2, part[1]).x, __builtin_bit_cast(uint2, part[1]).y));
+  };
+  // softmax weights e = 2w, 2w+1 (w < 4) of query block qb, rounded to bf16
+  // and packed: word w of the B operand of its PV
+  auto exp_word = [&](const f32x4 (&sacc)[QB][2], int qb, int w) __attribute__((always_inline)) -> uint32_t {
+    const int kk = w >> 1, i = 2 * (w & 1);
+    const float m = mref[qb];
+    return rkv::pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sacc[qb][kk][i], c, -m)),
+                            __builtin_amdgcn_exp2f(fmaf(sacc[qb][kk][i + 1], c, -m)));
+  };
+  // row maximum of query block qb over a half tile whose first key is key0
+  // (causal mask first when MASK): this lane's 8 scores, then the 4 lane
+  // groups of the query
+  auto lane_max = [&](f32x4 (&sacc)[QB][2], int qb, int key0, auto mask_tag) __attribute__((always_inline)) -> float {
+    if constexpr (decltype(mask_tag)::value) {
+      const int lim = qlim[qb] - key0;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const float mn = fmaxf(mref[qb], mt[qb]);
-        const float alpha = __builtin_amdgcn_exp2f(mref[qb] - mn);
-        mref[qb] = mn;
-        lacc[qb] *= alpha;
+      for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int db = 0; db < DBLK; ++db) oacc[qb][db] *= alpha;
-      }
+        for (int i = 0; i < 4; ++i)
+          if (4 * kk + i > lim) sacc[qb][kk][i] = -INFINITY;
     }
-    // QK of the next tile, with the gathers of K(t+2) and V(t+1) spread
-    // over its contraction steps
-    if constexpr (NEXT) qk(NPAR{}, s_nxt, std::true_type{}, tile + 2);
-    bf16x8 pb[2][2];
+    // three-input maxima: 8 values in 4 instructions
+    const float m1 = fmaxf(fmaxf(sacc[qb][0][0], sacc[qb][0][1]), sacc[qb][0][2]);
+    const float m2 = fmaxf(fmaxf(sacc[qb][0][3], sacc[qb][1][0]), sacc[qb][1][1]);
+    const float m3 = fmaxf(fmaxf(m1, m2), sacc[qb][1][2]);
+    return fmaxf(m3, sacc[qb][1][3]);
+  };
+  // raw row maximum of the latest half tile; the reference is raised when
+  // mx * c > mref + threshold, i.e. mx > thr = (mref + threshold) / c (c > 0),
+  // so the common case costs one compare
+  auto row_max = [&](float mx, int qb) __attribute__((always_inline)) -> bool {
+    mx = rkv::max_xor16(mx);
+    mx = rkv::max_xor32(mx);
+    mt[qb] = mx;
+    return mx > thr[qb];
+  };
+
+  // ---- one half-tile block, software pipelined in stages separated by
+  //      scheduling fences (operands are fetched two stages ahead and every
+  //      group of MFMAs has VALU work beside it, so the wave keeps the
+  //      matrix unit fed on its own and the SIMD's other wave fills gaps):
+  //   X: S^T(u+1) = K Q^T on half hk of the K tile in ks (QK), 2*KSTEPS
+  //      stages of QB MFMAs, beside the exponentials of half tile u
+  //      (scores s_old) and the gathers gj0 .. gj0+GPH-1 of K tile gk (into
+  //      kdst) and V tile gk-1 (into vdst) (GATHER);
+  //   Y: row sums and O^T += V^T P^T on half hv of the V tile in vs, DBLK
+  //      stages of QB MFMAs, beside the row maxima of half tile u+1 (QK)
+  //      whose first key is key0.
+  //   Returns whether some row's reference must be raised.
+  auto block = [&](const char* ks, int hk, f32x4 (&s_new)[QB][2], const f32x4 (&s_old)[QB][2],
+                   const char* vs, int hv, int key0, auto qk_tag, auto mask_tag, auto gather_tag, int gk,
+                   char* kdst, char* vdst, int gj0) __attribute__((always_inline)) -> bool {
+    constexpr bool QK = decltype(qk_tag)::value;
+    constexpr bool GATHER = decltype(gather_tag)::value;
+    constexpr int NK = 2 * KSTEPS;          // X stages
+    constexpr int WPS = 4 * QB / NK;        // exponential words per X stage
+    constexpr int NG = 2 * GPH;             // gathers of this block (K and V alternating)
+    static_assert(WPS * NK == 4 * QB, "exponential words split evenly over X");
+    // slots of this block's gathers (contiguous per lane)
+    const int32_t* kslots = SlK[gk & 3] + (wave * RPI + drow) * NDMA + gj0;
+    const int32_t* vslots = SlV[(gk - 1) & 3] + (wave * RPI + drow) * NDMA + gj0;
+    bf16x8 kop[NK];
+    if constexpr (QK) {
+      kop[0] = k_op(ks, hk, 0);
+      kop[1] = k_op(ks, hk, 1);
+    }
+    uint32_t wv[QB][4];
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const float m = mref[qb];
+    for (int i = 0; i < NK; ++i) {
+      if constexpr (QK) {
+        if (i + 2 < NK) kop[i + 2] = k_op(ks, hk, i + 2);
+        const int st = i >> 1, kk = i & 1;
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        uint32_t wv[4];
+        for (int qb = 0; qb < QB; ++qb)
+          s_new[qb][kk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              kop[i], qreg[qb][st], st == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s_new[qb][kk], 0, 0, 0);
+      }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int kb = 2 * cc + (e >> 1), i = 2 * (e & 1);
-          wv[e] = rkv::pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(s_cur[qb][kb][i], c, -m)),
-                                   __builtin_amdgcn_exp2f(fmaf(s_cur[qb][kb][i + 1], c, -m)));
+      for (int e = i * WPS; e < (i + 1) * WPS; ++e) wv[e >> 2][e & 3] = exp_word(s_old, e >> 2, e & 3);
+      if constexpr (GATHER) {
+#pragma unroll
+        for (int gi = i * NG / NK; gi < (i + 1) * NG / NK; ++gi) {
+          const int j = gj0 + (gi >> 1);
+          // out-of-range slots are clamped into the pool (the debug check
+          // runs beside the kernel)
+          const uint32_t slot = min((uint32_t)((gi & 1) ? vslots[gi >> 1] : kslots[gi >> 1]), P - 1);
+          const int R = dma_row(wave, j, drow);
+          if (gi & 1)
+            dma16(vg + (uint64_t)slot * slot_bytes + (dch ^ swz_v<CH>(R)) * 16, vdst + (wave * NDMA + j) * 1024);
+          else
+            dma16(kg + (uint64_t)slot * slot_bytes + (dch ^ swz_k<CH>(R)) * 16, kdst + (wave * NDMA + j) * 1024);
         }
-        pb[qb][cc] = __builtin_bit_cast(bf16x8, make_uint4(wv[0], wv[1], wv[2], wv[3]));
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    const char* vs = vbuf(par);
+    bf16x8 pb[QB];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < QB; ++qb)
+      pb[qb] = __builtin_bit_cast(bf16x8, make_uint4(wv[qb][0], wv[qb][1], wv[qb][2], wv[qb][3]));
+    bf16x8 vop[DBLK];
+    vop[0] = v_op(vs, hv, 0);
+    vop[1] = v_op(vs, hv, 1);
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
-        lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[qb][cc], lacc[qb], 0, 0, 0);
+    for (int qb = 0; qb < QB; ++qb)
+      lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[qb], lacc[qb], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    bool raise = false;
+    float lm[QB];
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) {
+      if (db + 2 < DBLK) vop[db + 2] = v_op(vs, hv, db + 2);
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        // V^T operand: two transposed reads of 4 keys each.  Lane p of group
-        // gq points at key row cc*32 + 8*gq + 4*hh + p/4, d = 16*db + 4*(p%4);
-        // lane i then receives keys [0..3] of that row run at d = 16*db + i.
-        v4i16 part[2];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int row = cc * 32 + gq * 8 + hh * 4 + (l16 >> 2);
-          const int d = db * 16 + 4 * (l16 & 3);
-          const char* ptr = vs + row * ROWB + ((((d >> 3) ^ swz_v<CH>(row))) << 4) + ((d & 7) << 1);
-          part[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((RKV_LDS v4i16*)ptr);
-        }
-        const bf16x8 va = __builtin_bit_cast(
-            bf16x8, make_uint4(__builtin_bit_cast(uint2, part[0]).x, __builtin_bit_cast(uint2, part[0]).y,
-                               __builtin_bit_cast(uint2, part[1]).x, __builtin_bit_cast(uint2, part[1]).y));
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          oacc[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[qb][cc], oacc[qb][db], 0, 0, 0);
+      for (int qb = 0; qb < QB; ++qb)
+        oacc[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[db], pb[qb], oacc[qb][db], 0, 0, 0);
+      if constexpr (QK) {
+        // the maxima of query blocks spread over the Y stages: the lane's
+        // part of block qb, then its cross-lane part a stage later
+        constexpr int SPQ = DBLK / QB;        // Y stages per query block (2 or 1)
+        const int qb = db / SPQ;
+        if (SPQ == 1 || db % SPQ == 0) lm[qb] = lane_max(s_new, qb, key0, mask_tag);
+        if (SPQ == 1 || db % SPQ == SPQ - 1) raise |= row_max(lm[qb], qb);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
+    return raise;
   };
 
-  // prologue: slots of tiles 0..2, K of tiles 0 and 1, V of tile 0
+  // scores of the even and the odd half tiles
+  f32x4 s_ev[QB][2], s_od[QB][2];
+
+  // prologue: slots of tiles 0..2; K tiles 0 and 1 (keys -32..95), V tile 0;
+  // QK of half tile 0 (the second half of K tile 0) and its maxima
   dma_slots(0);
   dma_slots(1);
   dma_slots(2);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  bad |= dma_k(0, I0{});
-  bad |= dma_v(0, I0{});
-  bad |= dma_k(1, I1{});
+  dma_k(0, I0{});
+  dma_v(0, I0{});
+  dma_k(1, I1{});
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  qk(I0{}, s_even, std::false_type{}, 0);
-  // iteration t (K(t+1), V(t) resident): DMA K(t+2), V(t+1) and the slots
-  // of tile t+3 while computing; then wait for them and meet at the barrier
-  auto iteration = [&](int tile, auto par) {
+#pragma unroll
+  for (int i = 0; i < 2 * KSTEPS; ++i) {
+    const bf16x8 ka = k_op(K0, 1, i);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+      s_ev[qb][i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          ka, qreg[qb][i >> 1], (i >> 1) == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s_ev[qb][i & 1], 0, 0, 0);
+  }
+  {
+    bool raise0 = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float lm = first_mask_tile == 0 ? lane_max(s_ev, qb, 0, std::true_type{})
+                                            : lane_max(s_ev, qb, 0, std::false_type{});
+      raise0 |= row_max(lm, qb);
+    }
+    if (__builtin_amdgcn_ballot_w64(raise0)) rescale(mt);
+  }
+
+  // iteration t (half tile 2t's maxima taken; K tile t+1 = half tiles 2t+1
+  // and 2t+2, V tile t = half tiles 2t and 2t+1 resident): two blocks
+  //   exp(2t) || QK(2t+1), then PV(2t) || max(2t+1)
+  //   exp(2t+1) || QK(2t+2), then PV(2t+1) || max(2t+2)
+  // with the gathers of K tile t+2 and V tile t+1 spread over the two QK
+  // phases, then wait for them and meet at the barrier.  MASK covers both
+  // maxima taken here (half tiles of tiles t and t+1); on a fully visible
+  // half tile the mask changes nothing.  Without NEXT (the last tile) there
+  // is no half tile 2t+2 and nothing to gather.
+  auto iteration = [&](int tile, auto par, auto mask_tag, auto next_tag) __attribute__((always_inline)) {
+    constexpr bool NEXT = decltype(next_tag)::value;
+    using NPAR = std::integral_constant<int, 1 - decltype(par)::value>;
+    using GT = std::integral_constant<bool, NEXT>;
     // The slot indices of tile t+3 go straight from the table into their
-    // LDS stage (wave 0, one 4-byte DMA; they are range-checked where the
+    // LDS stage (one 4-byte DMA per wave; they are range-checked where the
     // gathers read them), so no register has to wait for them.  Past the
     // last tile the keys are clamped: the gathers then refill the stage
     // consumed in the previous iteration with rows nobody reads again.
     dma_slots(tile + 3);
-    const bool next = tile + 1 < ntiles;
-    if (tile < first_mask_tile) {
-      if (next) step(tile, par, std::false_type{}, std::true_type{});
-      else step(tile, par, std::false_type{}, std::false_type{});
-    } else {
-      if (next) step(tile, par, std::true_type{}, std::true_type{});
-      else step(tile, par, std::true_type{}, std::false_type{});
+    char* kn = kbuf(NPAR{});      // K tile t+1
+    char* kd = kbuf(par);         // K tile t+2 lands in the stage K tile t used
+    char* vs = vbuf(par);         // V tile t
+    char* vd = vbuf(NPAR{});      // V tile t+1
+    bool up = block(kn, 0, s_od, s_ev, vs, 0, tile * BN + 32, std::true_type{}, mask_tag, GT{}, tile + 2, kd, vd, 0);
+    if (__builtin_amdgcn_ballot_w64(up)) rescale(mt);
+    up = block(kn, 1, s_ev, s_od, vs, 1, tile * BN + BN, GT{}, mask_tag, GT{}, tile + 2, kd, vd, GPH);
+    if constexpr (NEXT) {
+      if (__builtin_amdgcn_ballot_w64(up)) rescale(mt);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
   for (int tile = 0; tile < ntiles; tile += 2) {
-    iteration(tile, I0{});
-    if (tile + 1 < ntiles) iteration(tile + 1, I1{});
+    const bool m0 = tile + 1 >= first_mask_tile, n0 = tile + 1 < ntiles;
+    if (m0) {
+      if (n0) iteration(tile, I0{}, std::true_type{}, std::true_type{});
+      else iteration(tile, I0{}, std::true_type{}, std::false_type{});
+    } else {
+      iteration(tile, I0{}, std::false_type{}, std::true_type{});
+    }
+    if (tile + 1 < ntiles) {
+      const bool m1 = tile + 2 >= first_mask_tile, n1 = tile + 2 < ntiles;
+      if (m1) {
+        if (n1) iteration(tile + 1, I1{}, std::true_type{}, std::true_type{});
+        else iteration(tile + 1, I1{}, std::true_type{}, std::false_type{});
+      } else {
+        iteration(tile + 1, I1{}, std::false_type{}, std::true_type{});
+      }
+    }
   }
-  if (a.err && bad) rkv::raise_flag(a.err);
 
   // ---- epilogue: lane holds o[query l16][d = db*16 + 4*gq + 0..3]
   uint16_t* obase = (uint16_t*)a.o;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const float lsum = lacc[qb][0];
     if (!qvalid[qb]) continue;
     const float inv = 1.f / lsum;
@@ -486,6 +604,21 @@ __global__ __launch_bounds__(256, 2) void extend_bf16(ExtendArgs a) {
     if (a.lse && gq == 0)
       a.lse[(int64_t)qtok[qb] * a.hq + qhead[qb]] = (mref[qb] + log2f(lsum)) * 0.69314718055994531f;
   }
+}
+
+// Debug check beside the bf16 kernel, which clamps every gathered slot into
+// the pool: one workgroup per request over the table entries of the keys it
+// reads, [0, p + n) (within ld); an entry outside [0, pool_slots) raises the
+// flag.
+__global__ __launch_bounds__(256) void check_slots(ExtendArgs a) {
+  const int r = blockIdx.x;
+  if (r >= a.B) return;
+  const int64_t n = (int64_t)a.qo_indptr[r + 1] - a.qo_indptr[r];
+  const int64_t L = min((int64_t)a.prefix_lens[r] + n, a.ld);
+  const int32_t* row = a.r2t + (int64_t)r * a.ld;
+  bool bad = false;
+  for (int64_t i = threadIdx.x; i < L; i += blockDim.x) bad |= (uint32_t)row[i] >= (uint64_t)a.pool_slots;
+  if (bad) rkv::raise_flag(a.err);
 }
 
 // fp32: one wave per (query row, q head).  Lanes split D; keys are walked in
@@ -592,10 +725,11 @@ extern "C" int rkv_attn_extend(const void* q, const void* k_pool, const void* v_
     int64_t grid = a.tiles_bound * hkv;
     grid = (grid + rkv::kXcds - 1) / rkv::kXcds * rkv::kXcds;
     if (grid > 0x7fffffff) return rkv::fail(RKV_ENOTSUP, "rkv_attn_extend: grid too large");
+    if (a.err) hipLaunchKernelGGL(check_slots, dim3((unsigned)B), dim3(256), 0, st, a);
     if (d == 128)
-      hipLaunchKernelGGL(extend_bf16<128>, dim3((unsigned)grid), dim3(256), 0, st, a);
+      hipLaunchKernelGGL(extend_bf16<128>, dim3((unsigned)grid), dim3(NWAVES * 64), 0, st, a);
     else
-      hipLaunchKernelGGL(extend_bf16<64>, dim3((unsigned)grid), dim3(256), 0, st, a);
+      hipLaunchKernelGGL(extend_bf16<64>, dim3((unsigned)grid), dim3(NWAVES * 64), 0, st, a);
   } else {
     a.tiles_bound = 0;
     const int64_t waves = total_new * hq;
