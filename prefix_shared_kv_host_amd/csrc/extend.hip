@@ -26,8 +26,8 @@
 //     runs one half tile ahead of PV while an iteration still consumes one K
 //     and one V tile.  K runs two tiles ahead, V one; the slot indices reach
 //     LDS by 4-byte DMA straight from the table, one more tile ahead.  The
-//     gathers of a tile are spread over the QK stages of the iteration
-//     before.  K is read as 16-byte rows (ds_read_b128); V stays row-major
+//     gathers of a tile are spread over the first QK stages of the
+//     iteration before.  K is read as 16-byte rows (ds_read_b128); V stays row-major
 //     and the V^T operand comes from transposed reads (ds_read_b64_tr_b16).
 //     Gathered slots are clamped into the pool; a separate check kernel,
 //     launched only in debug mode, reports table entries outside it.
@@ -157,16 +157,20 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 // of this file's kernels goes through these two, so no compiler-generated
 // code there keeps a value in M0 across them (the compiler warns that a
 // clobbered M0 is reserved; nothing of its own relies on M0 here).
+// The LDS address is the low half of the generic address: the shared
+// aperture is 4 GiB aligned, so that half is the LDS offset itself (a cast
+// to the LDS address space would add a null test per copy).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const void* g, const void* lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(g), "s"(__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(RKV_LDS void*)lds_base))
+               :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_base)))
                : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void* g, const void* lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
-               :: "v"(g), "s"(__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(RKV_LDS void*)lds_base))
+               :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_base)))
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -185,9 +189,7 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void extend_bf16(ExtendArgs a) {
   constexpr int DBLK = D / 16;             // PV output blocks
   constexpr int RPI = 1024 / ROWB;         // rows one wave moves per DMA instruction
   constexpr int NDMA = BN / (RPI * NWAVES);  // DMA instructions per wave per tile (each of K, V)
-  constexpr int GPH = NDMA / 2;            // of those, issued in each half-tile QK phase
   constexpr int TILEB = BN * ROWB;         // bytes of one K or V tile
-  static_assert(GPH * 2 == NDMA && GPH >= 1, "the gathers of a tile split over its two QK phases");
 
   // K runs one tile ahead of V, each in two stages; slot indices run one
   // more tile ahead.  The stages are separate LDS objects addressed with a
@@ -331,17 +333,19 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void extend_bf16(ExtendArgs a) {
   // s[qb][kk] holds, for lane group gq, the keys 8*gq + 4*kk + [0..3] of the
   // half tile for its query (K rows are placed in LDS so).
 
-  // raw row maxima of the latest half tile, and the raise thresholds
+  // this lane's part of the raw row maxima of the latest half tile, and the
+  // raise thresholds
   float mt[QB], thr[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) thr[qb] = -INFINITY;
-  // the rare rescale: raise the reference of every row of the wave that
-  // needs it and rescale its O and row sum (PV of the previous half tile
-  // has been issued)
+  // the rare rescale: raise the reference of every row of the wave to its
+  // row maximum (the 4 lane groups' parts) and rescale its O and row sum (PV
+  // of the previous half tile has been issued)
   auto rescale = [&](const float (&mtv)[QB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const float mn = fmaxf(mref[qb], mtv[qb] * c);
+      const float rmx = rkv::max_xor32(rkv::max_xor16(mtv[qb]));
+      const float mn = fmaxf(mref[qb], rmx * c);
       const float alpha = __builtin_amdgcn_exp2f(mref[qb] - mn);
       mref[qb] = mn;
       thr[qb] = (mn + kRescaleThreshold) / c;
@@ -401,12 +405,12 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void extend_bf16(ExtendArgs a) {
     const float m3 = fmaxf(fmaxf(m1, m2), sacc[qb][1][2]);
     return fmaxf(m3, sacc[qb][1][3]);
   };
-  // raw row maximum of the latest half tile; the reference is raised when
-  // mx * c > mref + threshold, i.e. mx > thr = (mref + threshold) / c (c > 0),
-  // so the common case costs one compare
+  // the reference is raised when the raw row maximum mx of the latest half
+  // tile has mx * c > mref + threshold, i.e. mx > thr = (mref + threshold) / c
+  // (c > 0).  A row's maximum exceeds thr exactly when one of its 4 lanes'
+  // parts does, so the common case costs one compare per lane and a ballot;
+  // the cross-lane maximum is taken only in the rescale.
   auto row_max = [&](float mx, int qb) __attribute__((always_inline)) -> bool {
-    mx = rkv::max_xor16(mx);
-    mx = rkv::max_xor32(mx);
     mt[qb] = mx;
     return mx > thr[qb];
   };
@@ -417,24 +421,24 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void extend_bf16(ExtendArgs a) {
   //      matrix unit fed on its own and the SIMD's other wave fills gaps):
   //   X: S^T(u+1) = K Q^T on half hk of the K tile in ks (QK), 2*KSTEPS
   //      stages of QB MFMAs, beside the exponentials of half tile u
-  //      (scores s_old) and the gathers gj0 .. gj0+GPH-1 of K tile gk (into
-  //      kdst) and V tile gk-1 (into vdst) (GATHER);
+  //      (scores s_old) and, with GATHER, all gathers of K tile gk (into
+  //      kdst) and V tile gk-1 (into vdst), one per stage;
   //   Y: row sums and O^T += V^T P^T on half hv of the V tile in vs, DBLK
   //      stages of QB MFMAs, beside the row maxima of half tile u+1 (QK)
   //      whose first key is key0.
   //   Returns whether some row's reference must be raised.
   auto block = [&](const char* ks, int hk, f32x4 (&s_new)[QB][2], const f32x4 (&s_old)[QB][2],
                    const char* vs, int hv, int key0, auto qk_tag, auto mask_tag, auto gather_tag, int gk,
-                   char* kdst, char* vdst, int gj0) __attribute__((always_inline)) -> bool {
+                   char* kdst, char* vdst) __attribute__((always_inline)) -> bool {
     constexpr bool QK = decltype(qk_tag)::value;
     constexpr bool GATHER = decltype(gather_tag)::value;
     constexpr int NK = 2 * KSTEPS;          // X stages
     constexpr int WPS = 4 * QB / NK;        // exponential words per X stage
-    constexpr int NG = 2 * GPH;             // gathers of this block (K and V alternating)
+    constexpr int NG = 2 * NDMA;            // gathers of this block (K and V alternating)
     static_assert(WPS * NK == 4 * QB, "exponential words split evenly over X");
     // slots of this block's gathers (contiguous per lane)
-    const int32_t* kslots = SlK[gk & 3] + (wave * RPI + drow) * NDMA + gj0;
-    const int32_t* vslots = SlV[(gk - 1) & 3] + (wave * RPI + drow) * NDMA + gj0;
+    const int32_t* kslots = SlK[gk & 3] + (wave * RPI + drow) * NDMA;
+    const int32_t* vslots = SlV[(gk - 1) & 3] + (wave * RPI + drow) * NDMA;
     bf16x8 kop[NK];
     if constexpr (QK) {
       kop[0] = k_op(ks, hk, 0);
@@ -457,7 +461,7 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void extend_bf16(ExtendArgs a) {
       if constexpr (GATHER) {
 #pragma unroll
         for (int gi = i * NG / NK; gi < (i + 1) * NG / NK; ++gi) {
-          const int j = gj0 + (gi >> 1);
+          const int j = gi >> 1;
           // out-of-range slots are clamped into the pool (the debug check
           // runs beside the kernel)
           const uint32_t slot = min((uint32_t)((gi & 1) ? vslots[gi >> 1] : kslots[gi >> 1]), P - 1);
@@ -491,7 +495,7 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void extend_bf16(ExtendArgs a) {
         oacc[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[db], pb[qb], oacc[qb][db], 0, 0, 0);
       if constexpr (QK) {
         // the maxima of query blocks spread over the Y stages: the lane's
-        // part of block qb, then its cross-lane part a stage later
+        // part of block qb, then its compare a stage later
         constexpr int SPQ = DBLK / QB;        // Y stages per query block (2 or 1)
         const int qb = db / SPQ;
         if (SPQ == 1 || db % SPQ == 0) lm[qb] = lane_max(s_new, qb, key0, mask_tag);
@@ -540,8 +544,10 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void extend_bf16(ExtendArgs a) {
   // and 2t+2, V tile t = half tiles 2t and 2t+1 resident): two blocks
   //   exp(2t) || QK(2t+1), then PV(2t) || max(2t+1)
   //   exp(2t+1) || QK(2t+2), then PV(2t+1) || max(2t+2)
-  // with the gathers of K tile t+2 and V tile t+1 spread over the two QK
-  // phases, then wait for them and meet at the barrier.  MASK covers both
+  // with the gathers of K tile t+2 and V tile t+1 spread over the first QK
+  // phase (as early as their stages are free: issuing half of them in the
+  // second phase left the end-of-iteration wait exposed), then wait for them
+  // and meet at the barrier.  MASK covers both
   // maxima taken here (half tiles of tiles t and t+1); on a fully visible
   // half tile the mask changes nothing.  Without NEXT (the last tile) there
   // is no half tile 2t+2 and nothing to gather.
@@ -559,9 +565,9 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void extend_bf16(ExtendArgs a) {
     char* kd = kbuf(par);         // K tile t+2 lands in the stage K tile t used
     char* vs = vbuf(par);         // V tile t
     char* vd = vbuf(NPAR{});      // V tile t+1
-    bool up = block(kn, 0, s_od, s_ev, vs, 0, tile * BN + 32, std::true_type{}, mask_tag, GT{}, tile + 2, kd, vd, 0);
+    bool up = block(kn, 0, s_od, s_ev, vs, 0, tile * BN + 32, std::true_type{}, mask_tag, GT{}, tile + 2, kd, vd);
     if (__builtin_amdgcn_ballot_w64(up)) rescale(mt);
-    up = block(kn, 1, s_ev, s_od, vs, 1, tile * BN + BN, GT{}, mask_tag, GT{}, tile + 2, kd, vd, GPH);
+    up = block(kn, 1, s_ev, s_od, vs, 1, tile * BN + BN, GT{}, mask_tag, std::false_type{}, tile + 2, kd, vd);
     if constexpr (NEXT) {
       if (__builtin_amdgcn_ballot_w64(up)) rescale(mt);
     }
