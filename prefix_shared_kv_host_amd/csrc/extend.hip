@@ -387,9 +387,9 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void extend_bf16(ExtendArgs a) {
     return rkv::pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sacc[qb][kk][i], c, -m)),
                             __builtin_amdgcn_exp2f(fmaf(sacc[qb][kk][i + 1], c, -m)));
   };
-  // row maximum of query block qb over a half tile whose first key is key0
-  // (causal mask first when MASK): this lane's 8 scores, then the 4 lane
-  // groups of the query
+  // this lane's part of the row maximum of query block qb over a half tile
+  // whose first key is key0 (causal mask first when MASK): the maximum of
+  // its 8 scores
   auto lane_max = [&](f32x4 (&sacc)[QB][2], int qb, int key0, auto mask_tag) __attribute__((always_inline)) -> float {
     if constexpr (decltype(mask_tag)::value) {
       const int lim = qlim[qb] - key0;
