@@ -690,13 +690,26 @@ def cpu_baseline():
                                             note="8 of the 64 extend requests of the 64/8-head batch"))
 
 
+LEGS = {
+    # leg: (config, phase index, prefix-shared decode)
+    "extend": ("c2", 1, False),
+    "decode": ("c3", 4, True),
+    "gqa-extend": ("c4", 2, False),
+    "gqa-decode": ("c4", 3, False),
+    "gqa-decode-cascade": ("c4", 3, True),
+}
+
+
 def one_leg(leg, steps, warmup):
-    """One kernel's workload of the step, timed alone with HIP events on the
-    launch stream: `steps` launches after `warmup`, each synchronized."""
+    """One kernel's workload, timed alone with HIP events on the launch
+    stream: `steps` launches after `warmup`, each synchronized.  extend and
+    decode are the step's two halves; the gqa-* legs are the 64/8-head
+    batch's (plain or prefix-shared decode), for counter passes."""
     import torch
     from inputs import configs
-    ph = Phase(leg, configs.c2, 1) if leg == "extend" else Phase(leg, configs.c3, 4)
-    if leg == "decode":
+    cfg, idx, cascade = LEGS[leg]
+    ph = Phase(leg, getattr(configs, cfg), idx)
+    if cascade:
         ph.use_cascade()
     stream = torch.cuda.current_stream()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
@@ -712,12 +725,18 @@ def one_leg(leg, steps, warmup):
     tb, s_ = ph.batch.host, ph.shape
     us = float(np.mean(at)) * 1e3
     out = dict(leg=leg, steps=steps, warmup=warmup, attend_us=us, scatter_us=float(np.mean(sc)) * 1e3)
-    if leg == "extend":
+    if ph.kind == "extend":
         F = extend_flops(tb["prefix_lens"], tb["seq_lens"], s_.hq, s_.d)
         out.update(flop=F, tflops=F / (us * 1e-6) / 1e12, frac_of_peak=F / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS)
-    else:
+    elif cascade:
         Bp = ph.plan_bytes()
         out.update(bytes_plan=Bp, gbs_plan=Bp / (us * 1e-6) / 1e9, frac_of_peak=Bp / (us * 1e-6) / 1e9 / PEAK_HBM_GBS)
+    else:
+        uniq = len(np.unique(np.concatenate([tb["req_to_token"][r][: tb["seq_lens"][r]]
+                                             for r in range(len(tb["seq_lens"]))])))
+        Bu = decode_bytes(tb["seq_lens"], s_.hq, s_.hkv, s_.d, 2, unique_slots=uniq)
+        out.update(bytes_unique=Bu, gbs_unique=Bu / (us * 1e-6) / 1e9,
+                   frac_of_peak_unique=Bu / (us * 1e-6) / 1e9 / PEAK_HBM_GBS)
     return out
 
 
@@ -728,10 +747,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-reps", type=int, default=10)
-    ap.add_argument("--leg", choices=["extend", "decode"], default=None,
-                    help="time one kernel's workload of the step alone (for counter runs under rocprofv3): "
+    ap.add_argument("--leg", choices=sorted(LEGS), default=None,
+                    help="time one kernel's workload alone (for counter runs under rocprofv3): "
                          "extend = scatter + attn_extend of the 64 x (1024 + 128) batch, decode = scatter + "
-                         "prefix-shared decode of the 256-request tree batch; prints one JSON line")
+                         "prefix-shared decode of the 256-request tree batch; gqa-extend, gqa-decode, "
+                         "gqa-decode-cascade = the 64/8-head batch's extend, plain decode and prefix-shared "
+                         "decode; prints one JSON line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this path has no sharding or collectives "

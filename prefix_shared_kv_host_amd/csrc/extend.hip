@@ -85,18 +85,22 @@ struct ExtendArgs {
 // request by request, in request order or in a.order's).  Wave-parallel
 // prefix sum over the requests; the result is uniform across the wave.
 // Returns false when tg is past the end.  An a.order entry outside [0, B)
-// owns no tiles.
-__device__ bool locate_tile(const ExtendArgs& a, int64_t tg, int& r, int& t) {
+// owns no tiles.  The request's first q row, new-token count and prefix
+// length come back with it: every lane loads them for its own request in the
+// same pass, so they cost no further dependent memory round trip.
+__device__ bool locate_tile(const ExtendArgs& a, int64_t tg, int& r, int& t, int& q0, int& n, int& p) {
   const int lane = threadIdx.x & 63;
   int64_t acc = 0;
   for (int base = 0; base < a.B; base += 64) {
     const int i = base + lane;
-    int c = 0, ri = i;
+    int c = 0, ri = i, q0i = 0, ni = 0, pi = 0;
     if (i < a.B) {
       if (a.order) ri = a.order[i];
       if ((unsigned)ri < (unsigned)a.B) {
-        const int64_t n = (int64_t)a.qo_indptr[ri + 1] - a.qo_indptr[ri];
-        c = (int)((n * a.G + BM - 1) / BM);
+        q0i = a.qo_indptr[ri];
+        ni = a.qo_indptr[ri + 1] - q0i;
+        pi = a.prefix_lens[ri];
+        c = (int)(((int64_t)ni * a.G + BM - 1) / BM);
       }
     }
     int s = c;
@@ -111,8 +115,12 @@ __device__ bool locate_tile(const ExtendArgs& a, int64_t tg, int& r, int& t) {
       const int first = __ffsll((long long)mask) - 1;
       const int s_first = __shfl(s, first);
       const int c_first = __shfl(c, first);
-      r = __shfl(ri, first);
-      t = (int)(tg - (acc + s_first - c_first));
+      // (uniform: readfirstlane keeps them in scalar registers)
+      r = __builtin_amdgcn_readfirstlane(__shfl(ri, first));
+      t = __builtin_amdgcn_readfirstlane((int)(tg - (acc + s_first - c_first)));
+      q0 = __builtin_amdgcn_readfirstlane(__shfl(q0i, first));
+      n = __builtin_amdgcn_readfirstlane(__shfl(ni, first));
+      p = __builtin_amdgcn_readfirstlane(__shfl(pi, first));
       return true;
     }
     acc += tot;
@@ -217,17 +225,14 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void extend_bf16(ExtendArgs a) {
   const int g = (int)(w / a.tiles_bound);
   const int64_t tg = w % a.tiles_bound;
   if (g >= a.hkv) return;
-  int r = 0, t = 0;
-  if (!locate_tile(a, tg, r, t)) return;
+  int r = 0, t = 0, q0 = 0, n = 0, p = 0;
+  if (!locate_tile(a, tg, r, t, q0, n, p)) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15;
   const int gq = lane >> 4;
-  const int q0 = a.qo_indptr[r];
-  const int n = a.qo_indptr[r + 1] - q0;
-  const int p = a.prefix_lens[r];
   const int G = a.G;
   const int rows_total = n * G;
   const int row0 = t * BM;
