@@ -197,15 +197,25 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float* acc, floa
 //     (member request, q head) pairs, up to CB blocks of 16, and every block
 //     reuses the same K operands and the same V tile.
 // One wave walks its keys 32 at a time:
-//   * each lane gathers the 16-byte pieces of its two K rows straight into
-//     MFMA A operands (registers, one step ahead);
+//   * the 32 K rows are copied global -> LDS as whole rows by 16-byte DMA
+//     into one K stage (KLDS: the matrix-core kernels), read back as MFMA A
+//     operands (ds_read_b128) by the score products, and refilled for the
+//     next step as soon as those products have their operands.  Whole rows
+//     per instruction halve the L1 requests per byte against the other form,
+//     where each lane gathers the 16-byte pieces of its two K rows straight
+//     into registers (64 bytes of a row per instruction, half a cache line):
+//     measured, the L1's request handling bounded that form (64/8-head
+//     decode 234 -> 219 us plain, 227 -> 214 us prefix-shared; the 8/1-head
+//     share 39 -> 33 us).  The register form stays for the shared items of
+//     the vector kernel's prefix-shared variant, whose LDS holds four waves'
+//     V stages and no more;
 //   * the 32 V rows are copied global -> LDS by 16-byte DMA (two stages) and
 //     read transposed (ds_read_b64_tr_b16) as the V^T operand of O^T += V^T P^T;
 //   * K rows are assigned so that a lane's S^T accumulators hold 8 consecutive
 //     keys, which is its slice of the bf16 P^T operand;
 //   * fp32 online softmax in the log2 domain, row sums on the MFMA.
-// Memory traffic is the same as the vector kernel's for one block; the
-// arithmetic moves from VALU FMAs (8 per head per element) to the matrix cores.
+// Bytes moved are the vector kernel's for one block; the arithmetic moves
+// from VALU FMAs (8 per head per element) to the matrix cores.
 namespace gqa {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -233,10 +243,24 @@ struct State {
 // operand of block cb (columns l16, rows d = k*32 + 8*gq + [0..7]).  Blocks
 // cb >= ncb (wave-uniform) are skipped.  Every gather is clamped into the
 // range and into the pool.  VSTREAM: the V tiles are fetched non-temporally.
-template <int D, int CB, bool VSTREAM>
+// LDS DMA issued from assembly (lane l's 16 bytes land at lds + 16*l): the
+// compiler then keeps no lgkmcnt bookkeeping for it and does not drain the
+// operand reads fetched ahead; every stage it fills is read only after a full
+// s_waitcnt by the same wave.  The LDS address is the low half of the generic
+// address (the shared aperture is 4 GiB aligned).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* g, const void* lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds))
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int D, int CB, bool VSTREAM, bool KLDS>
 __device__ __forceinline__ void walk(const DecodeArgs& a, const int32_t* row_tab, int k_begin, int k_end, int g,
                                      const bf16x8 (&q)[CB][D / 32], int ncb, State<D, CB>& st, char* V0,
-                                     char* V1) {
+                                     char* V1, char* KS) {
   constexpr int ROWB = D * 2;
   constexpr int CH = D / 8;
   constexpr int KSTEPS = D / 32;
@@ -251,7 +275,7 @@ __device__ __forceinline__ void walk(const DecodeArgs& a, const int32_t* row_tab
 
   const uint32_t P = (uint32_t)min(a.pool_slots, (int64_t)0x7fffffff);
   const uint32_t slot_bytes = (uint32_t)a.hkv * ROWB;
-  const char* kg = (const char*)a.kp + (uint64_t)g * ROWB + gq * 16;
+  const char* kg = (const char*)a.kp + (uint64_t)g * ROWB + (KLDS ? 0 : gq * 16);
   const char* vg = (const char*)a.vp + (uint64_t)g * ROWB;
   // lane (lane & 31) loads the slot of key base + (lane & 31).  Its range
   // check (checked) is taken where the slots are used, one step later: a
@@ -264,16 +288,37 @@ __device__ __forceinline__ void walk(const DecodeArgs& a, const int32_t* row_tab
     }
     return slot;
   };
-  // K operands of one step; refilled for the next step as soon as the
-  // score products have read them
+  // K operands of one step (register form); refilled for the next step as
+  // soon as the score products have read them
   uint4 kreg[2][KSTEPS];
   auto load_k = [&](int32_t slots) {
+    if constexpr (KLDS) {
+      // whole 256-byte rows into the K stage: LDS row R = 16*kb + m holds
+      // the key feeding MFMA row m of block kb, its 16-byte chunks XORed
+      // with the row so that a 16-row operand read is conflict-free
+      const int drow = lane / CH, dch = lane % CH;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int32_t sl = __shfl(slots, key_of(kb, l16));
-      const char* rowp = kg + (uint64_t)(uint32_t)sl * slot_bytes;
+      for (int j = 0; j < NDMA; ++j) {
+        const int R = j * RPI + drow;
+        const int32_t sl = __shfl(slots, key_of(R >> 4, R & 15));
+        dma16(kg + (uint64_t)(uint32_t)sl * slot_bytes + ((dch ^ (R & (CH - 1))) << 4), KS + j * 1024);
+      }
+    } else {
 #pragma unroll
-      for (int k = 0; k < KSTEPS; ++k) kreg[kb][k] = load_kv<false>(rowp + k * 64);
+      for (int kb = 0; kb < 2; ++kb) {
+        const int32_t sl = __shfl(slots, key_of(kb, l16));
+        const char* rowp = kg + (uint64_t)(uint32_t)sl * slot_bytes;
+#pragma unroll
+        for (int k = 0; k < KSTEPS; ++k) kreg[kb][k] = load_kv<false>(rowp + k * 64);
+      }
+    }
+  };
+  auto k_op = [&](int kb, int k) -> bf16x8 {
+    if constexpr (KLDS) {
+      const int R = kb * 16 + l16;
+      return __builtin_bit_cast(bf16x8, *(const uint4*)(KS + R * ROWB + (((4 * k + gq) ^ (R & (CH - 1))) << 4)));
+    } else {
+      return __builtin_bit_cast(bf16x8, kreg[kb][k]);
     }
   };
   auto dma_v = [&](int32_t slots, char* dst) {
@@ -287,8 +332,8 @@ __device__ __forceinline__ void walk(const DecodeArgs& a, const int32_t* row_tab
                                        (RKV_LDS void*)(dst + j * 1024), 16, 0, VSTREAM ? kNonTemporal : 0);
     }
   };
-  // K(k_begin) in registers and V(k_begin) in stage V0; the slots of each
-  // next step are fetched a step ahead
+  // K(k_begin) in the K stage (or registers) and V(k_begin) in stage V0; the
+  // slots of each next step are fetched a step ahead
   {
     const int32_t s0 = checked(fetch(k_begin));
     load_k(s0);
@@ -296,9 +341,9 @@ __device__ __forceinline__ void walk(const DecodeArgs& a, const int32_t* row_tab
   }
   int32_t nslot = 0;
   if (k_begin + STEP < k_end) nslot = fetch(k_begin + STEP);
-  // One 32-key step on the K operands in kreg and the V tile in `cur`; with
-  // LOAD it issues the next step's gathers (K into kreg once the score
-  // products have read it, V into `nxt`).  The stages are fixed at compile
+  // One 32-key step on the K operands (K stage or kreg) and the V tile in
+  // `cur`; with LOAD it issues the next step's gathers (K once the score
+  // products have read theirs, V into `nxt`).  The stages are fixed at compile
   // time, and the loads happen unconditionally inside a step, so that
   // nothing waits for a gather it does not read:
   //   - with a run-time LDS stage index the compiler cannot tell the
@@ -323,8 +368,7 @@ __device__ __forceinline__ void walk(const DecodeArgs& a, const int32_t* row_tab
         sacc[cb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k = 0; k < KSTEPS; ++k)
-          sacc[cb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[kb][k]), q[cb][k],
-                                                                 sacc[cb][kb], 0, 0, 0);
+          sacc[cb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_op(kb, k), q[cb][k], sacc[cb][kb], 0, 0, 0);
       }
     }
     if constexpr (LOAD) {
@@ -431,7 +475,7 @@ __device__ __forceinline__ void store_partial(float* dst, const f32x4 (&o)[D / 1
 }  // namespace gqa
 
 template <int D, bool VSTREAM>
-__device__ __forceinline__ void gqa_item(const DecodeArgs& a, int64_t w, char* V0, char* V1) {
+__device__ __forceinline__ void gqa_item(const DecodeArgs& a, int64_t w, char* V0, char* V1, char* KS) {
   using namespace gqa;
   const int s = (int)(w % a.splits);
   int64_t rest = w / a.splits;
@@ -453,7 +497,7 @@ __device__ __forceinline__ void gqa_item(const DecodeArgs& a, int64_t w, char* V
   for (int db = 0; db < D / 16; ++db) st.o[0][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   st.l[0] = f32x4{0.f, 0.f, 0.f, 0.f};
   st.m[0] = -INFINITY;
-  walk<D, 1, VSTREAM>(a, a.r2t + (int64_t)r * a.ld, k_begin, k_end, g, qreg, 1, st, V0, V1);
+  walk<D, 1, VSTREAM, true>(a, a.r2t + (int64_t)r * a.ld, k_begin, k_end, g, qreg, 1, st, V0, V1, KS);
   if (!hvalid) return;
   const float lsum = st.l[0][0];
   if (rec < 0) {
@@ -474,9 +518,9 @@ __device__ __forceinline__ void gqa_item(const DecodeArgs& a, int64_t w, char* V
 // by side on one XCD.  Column c = cb*16 + l16 is member c / G of the job and
 // q head g*G + c % G.  The plan's values are checked against the batch
 // before use; a job that does not fit is skipped (flag raised in debug mode).
-template <int D, int CB>
+template <int D, int CB, bool KLDS>
 __device__ __forceinline__ void shared_item(const DecodeArgs& a, const SharedJobs& j, int64_t w, char* V0,
-                                            char* V1) {
+                                            char* V1, char* KS) {
   using namespace gqa;
   const int job = (int)(w % j.n_jobs);
   const int g = (int)(w / j.n_jobs);
@@ -520,7 +564,7 @@ __device__ __forceinline__ void shared_item(const DecodeArgs& a, const SharedJob
     st.l[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
     st.m[cb] = -INFINITY;
   }
-  walk<D, CB, false>(a, a.r2t + (int64_t)rep * a.ld, kb, ke, g, qreg, ncb, st, V0, V1);
+  walk<D, CB, false, KLDS>(a, a.r2t + (int64_t)rep * a.ld, kb, ke, g, qreg, ncb, st, V0, V1, KS);
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     if (!valid[cb]) continue;
@@ -566,7 +610,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CB > 0 ? 2 
     if (b < shared_blocks) {
       const int wave = (int)(threadIdx.x >> 6);
       const int64_t item = rkv::xcd_work_item(b, shared_blocks) * 4 + wave;
-      if (item < (int64_t)j.n_jobs * a.hkv) shared_item<D, CB>(a, j, item, V0[wave], V1[wave]);
+      if (item < (int64_t)j.n_jobs * a.hkv) shared_item<D, CB, false>(a, j, item, V0[wave], V1[wave], nullptr);
       return;
     }
     w = rkv::xcd_work_item(b - shared_blocks, (int64_t)gridDim.x - shared_blocks);
@@ -743,13 +787,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CB > 0 ? 2 
   }
 }
 
-// Two waves per SIMD: without the hint the two-stage walk takes more than
-// 256 registers at D = 128 and runs one.
+// One wave per workgroup with 24 KB of LDS at D = 128 (two V stages and the
+// K stage): six waves per CU.  The hint caps the registers for two waves per
+// SIMD.
 template <int D>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_gqa(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char V0[32 * D * 2];
   __shared__ __attribute__((aligned(16))) char V1[32 * D * 2];
-  gqa_item<D, false>(a, rkv::xcd_work_item(blockIdx.x, gridDim.x), V0, V1);
+  __shared__ __attribute__((aligned(16))) char KS[32 * D * 2];
+  gqa_item<D, false>(a, rkv::xcd_work_item(blockIdx.x, gridDim.x), V0, V1, KS);
 }
 
 // Prefix-shared phase 1 in one launch when the tails run on the matrix
@@ -757,8 +803,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 // rest the tail splits, one wave per item, so the shared work (a few hundred
 // keys per item) overlaps the long private tails instead of running,
 // latency-bound, before them.  Each range has its own XCD-aware order.  Two
-// waves per SIMD: the register budget of 256 per lane holds CB = 2 at
-// D = 128 (without the hint the compiler takes more and runs one).
+// waves per SIMD at most (24 KB of LDS per wave at D = 128 allows six per
+// CU): the register budget of 256 per lane holds CB = 2 at D = 128 (without
+// the hint the compiler takes more and runs one).
 // TAIL_STREAM: the tails' V tiles come in by non-temporal DMA (their rows are
 // read by no other item); chosen by the host for launches with many tail
 // items (see launch_cascade_cb).
@@ -767,13 +814,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     DecodeArgs a, SharedJobs j, int32_t shared_blocks) {
   __shared__ __attribute__((aligned(16))) char V0[32 * D * 2];
   __shared__ __attribute__((aligned(16))) char V1[32 * D * 2];
+  __shared__ __attribute__((aligned(16))) char KS[32 * D * 2];
   const int b = (int)blockIdx.x;
   if (b < shared_blocks) {
     const int64_t w = rkv::xcd_work_item(b, shared_blocks);
-    if (w < (int64_t)j.n_jobs * a.hkv) shared_item<D, CB>(a, j, w, V0, V1);
+    if (w < (int64_t)j.n_jobs * a.hkv) shared_item<D, CB, true>(a, j, w, V0, V1, KS);
     return;
   }
-  gqa_item<D, TAIL_STREAM>(a, rkv::xcd_work_item(b - shared_blocks, (int64_t)gridDim.x - shared_blocks), V0, V1);
+  gqa_item<D, TAIL_STREAM>(a, rkv::xcd_work_item(b - shared_blocks, (int64_t)gridDim.x - shared_blocks), V0, V1, KS);
 }
 
 // Phase 2: one wave per (request, q head); lanes cover D.
