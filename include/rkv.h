@@ -322,9 +322,12 @@ int rkv_table_append(int32_t* req_to_token, int64_t ld, int32_t* seq_lens, const
  *   K_t = k_pool[req_to_token[r, t], h / (Hq/Hkv)],  V_t likewise,
  *   lse[row, h] = natural-log log-sum-exp of the scaled scores (fp32;
  *   `lse` may be NULL).
- * total_new must equal qo_indptr[B] (the number of q rows) and max_new must
- * be >= every n_r; together they size the grid (a smaller max_new leaves rows
- * of the longer requests unwritten).  The new tokens' K/V must already be in
+ * qo_indptr[0] must be 0, total_new must equal qo_indptr[B] (the number of
+ * q rows) and max_new must be >= every n_r; together they size the grid (a
+ * smaller max_new leaves rows of the longer requests unwritten).  When
+ * total_new == B * max_new every request has max_new new tokens, and the
+ * bf16 path takes request r's rows to start at r * max_new without reading
+ * qo_indptr.  The new tokens' K/V must already be in
  * the pool (rkv_kv_scatter). bf16: QK^T and PV on bf16 MFMA with fp32
  * accumulation, fp32 online
  * softmax, softmax weights rounded to bf16 for PV, o rounded to bf16 (RNE).

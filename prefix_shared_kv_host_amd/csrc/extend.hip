@@ -78,6 +78,8 @@ struct ExtendArgs {
   int64_t pool_slots;
   int64_t tiles_bound;      // work items per kv head
   int64_t total_new;        // q rows; rows at or past it are never read
+  int32_t uni_n;            // > 0: every request has this many new tokens
+  int64_t tiles_per_req;    // work items per request when uni_n > 0
   int* err;
 };
 
@@ -226,7 +228,25 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void extend_bf16(ExtendArgs a) {
   const int64_t tg = w % a.tiles_bound;
   if (g >= a.hkv) return;
   int r = 0, t = 0, q0 = 0, n = 0, p = 0;
-  if (!locate_tile(a, tg, r, t, q0, n, p)) return;
+  const bool uni = a.uni_n > 0;
+  if (uni) {
+    // every request has uni_n new tokens (so its q rows start at r * uni_n):
+    // the request and tile follow from the work item's index, and the
+    // prefix length is loaded beside the first slot indices and queries
+    // below instead of before them (one dependent memory round trip less)
+    const int64_t i = tg / a.tiles_per_req;
+    if (i >= a.B) return;
+    t = (int)(tg - i * a.tiles_per_req);
+    r = (int)i;
+    if (a.order) {
+      r = a.order[i];
+      if ((unsigned)r >= (unsigned)a.B) return;
+    }
+    n = a.uni_n;
+    q0 = r * n;
+  } else if (!locate_tile(a, tg, r, t, q0, n, p)) {
+    return;
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -237,35 +257,27 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void extend_bf16(ExtendArgs a) {
   const int rows_total = n * G;
   const int row0 = t * BM;
   const int row_last = min(row0 + BM, rows_total) - 1;
-  // keys never reach past the table row, whatever the lengths say
-  const int kv_end = (int)min((int64_t)p + row_last / G + 1, a.ld);
-  const int ntiles = (kv_end + BN - 1) / BN;
-  // tiles before this one are fully visible to every row of the workgroup
-  const int first_mask_tile = min(ntiles, (p + row0 / G) / BN);
 
-  // ---- queries of this wave: rows row0 + wave*32 + qb*16 + l16
+  // ---- queries of this wave: rows row0 + wave*32 + qb*16 + l16.  Every
+  //      lane loads a query (a row past the request's rows reads q row 0,
+  //      and a row whose position lies past the table row its own), so the
+  //      loads need no branch; only valid rows are written.
   bf16x8 qreg[QB][KSTEPS];
-  int qlim[QB], qhead[QB], qtok[QB];
+  int qlim[QB], qhead[QB], qtok[QB], qj[QB];
   bool qvalid[QB];
   const uint16_t* qbase = (const uint16_t*)a.q;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = row0 + wave * (QB * 16) + qb * 16 + l16;
-    qvalid[qb] = row < rows_total && (int64_t)q0 + row / G < a.total_new && p + row / G < kv_end;
-    const int j = qvalid[qb] ? row / G : 0;
-    const int hh = qvalid[qb] ? row % G : 0;
-    qtok[qb] = q0 + j;
+    const int j = row / G;
+    qvalid[qb] = row < rows_total && (int64_t)q0 + j < a.total_new;
+    qj[qb] = qvalid[qb] ? j : 0;
+    const int hh = qvalid[qb] ? row - j * G : 0;
+    qtok[qb] = q0 + qj[qb];
     qhead[qb] = g * G + hh;
-    // last visible key, relative to the first key this lane holds in a
-    // 32-key half tile
-    qlim[qb] = (qvalid[qb] ? p + j : kv_end - 1) - 8 * gq;
+    const uint16_t* qp = qbase + (qvalid[qb] ? ((int64_t)qtok[qb] * a.hq + qhead[qb]) * D : 0) + gq * 8;
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (qvalid[qb])
-        v = *(const uint4*)(qbase + ((int64_t)qtok[qb] * a.hq + qhead[qb]) * D + s * 32 + gq * 8);
-      qreg[qb][s] = __builtin_bit_cast(bf16x8, v);
-    }
+    for (int s = 0; s < KSTEPS; ++s) qreg[qb][s] = __builtin_bit_cast(bf16x8, *(const uint4*)(qp + s * 32));
   }
 
   f32x4 oacc[QB][DBLK];
@@ -285,9 +297,21 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void extend_bf16(ExtendArgs a) {
   const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
   const float c = a.scale_log2e;
 
-  // ---- gathers: every row index is clamped into [0, kv_end) and every slot
-  //      into [0, pool_slots), so no access leaves the table or the pool;
-  //      keys past kv_end are masked by the causal test
+  // keys never reach past the table row, whatever the lengths say; the
+  // bounds that follow from the prefix length are set once it has arrived
+  int kv_end = 0, ntiles = 0, first_mask_tile = 0;
+  auto set_bounds = [&]() {
+    kv_end = (int)min((int64_t)p + row_last / G + 1, a.ld);
+    ntiles = (kv_end + BN - 1) / BN;
+    // tiles before this one are fully visible to every row of the workgroup
+    first_mask_tile = min(ntiles, (p + row0 / G) / BN);
+  };
+  if (!uni) set_bounds();
+
+  // ---- gathers: every row index is clamped into the table row (into
+  //      [0, kv_end) once the prefix length is known) and every slot into
+  //      [0, pool_slots), so no access leaves the table or the pool; keys
+  //      past kv_end are masked by the causal test
   const int32_t* row_tab = a.r2t + (int64_t)r * a.ld;
   const uint32_t P = (uint32_t)min(a.pool_slots, (int64_t)0x7fffffff);
   const uint32_t slot_bytes = (uint32_t)a.hkv * ROWB;
@@ -303,32 +327,41 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void extend_bf16(ExtendArgs a) {
   const int key_v = pos_row(lane);
   const char* kg = (const char*)a.kp + (uint64_t)g * ROWB;
   const char* vg = (const char*)a.vp + (uint64_t)g * ROWB;
-  // gather instruction j of a tile (slot read from LDS just before it), so
-  // the gathers of a tile can be spread over the MFMA work instead of
-  // queueing behind one another at the start of an iteration; a slot
-  // outside [0, pool_slots) is clamped to the pool's last slot
-  auto gather1 = [&](const int32_t* slots, char* dst, const char* src, int j, auto is_k) {
-    const uint32_t slot = min((uint32_t)slots[(wave * RPI + drow) * NDMA + j], P - 1);
+  // A gather lane's NDMA slots of a tile are contiguous in the slot stage:
+  // one LDS read brings them all (the copies are assembly with a memory
+  // clobber, so a slot read between two of them would have to complete
+  // before the second could issue).
+  typedef int32_t slotv __attribute__((ext_vector_type(NDMA)));
+  auto lane_slots = [&](const int32_t* stage) -> slotv {
+    return *(const slotv*)(stage + (wave * RPI + drow) * NDMA);
+  };
+  // gather instruction j of a tile; a slot outside [0, pool_slots) is
+  // clamped to the pool's last slot
+  auto gather1 = [&](int32_t slot_in, char* dst, const char* src, int j, auto is_k) {
+    const uint32_t slot = min((uint32_t)slot_in, P - 1);
     const int R = dma_row(wave, j, drow);
     const int lch = dch ^ (decltype(is_k)::value ? swz_k<CH>(R) : swz_v<CH>(R));
     dma16(src + (uint64_t)slot * slot_bytes + lch * 16, dst + (wave * NDMA + j) * 1024);
   };
   auto dma_k = [&](int tile, auto par) {
+    const slotv sl = lane_slots(SlK[tile & 3]);
 #pragma unroll
-    for (int j = 0; j < NDMA; ++j) gather1(SlK[tile & 3], kbuf(par), kg, j, std::true_type{});
+    for (int j = 0; j < NDMA; ++j) gather1(sl[j], kbuf(par), kg, j, std::true_type{});
   };
   auto dma_v = [&](int tile, auto par) {
+    const slotv sl = lane_slots(SlV[tile & 3]);
 #pragma unroll
-    for (int j = 0; j < NDMA; ++j) gather1(SlV[tile & 3], vbuf(par), vg, j, std::false_type{});
+    for (int j = 0; j < NDMA; ++j) gather1(sl[j], vbuf(par), vg, j, std::false_type{});
   };
   // slot indices of tile `tile` into stage tile & 3 (wave 0 for K, wave 1
   // for V, one 4-byte DMA each, straight from the table; keys clamped into
-  // [0, kv_end)).  K tile k holds keys [64k - 32, 64k + 32): shifted half a
+  // [0, hi]).  K tile k holds keys [64k - 32, 64k + 32): shifted half a
   // tile against V, so that QK runs one half tile ahead of PV while each
   // iteration still reads one K tile and one V tile.
-  auto dma_slots = [&](int tile) {
-    if (wave == 0) dma4(row_tab + min(max(tile * BN - BN / 2 + key_k, 0), kv_end - 1), SlK[tile & 3]);
-    else if (wave == 1) dma4(row_tab + min(tile * BN + key_v, kv_end - 1), SlV[tile & 3]);
+  auto dma_slots = [&](int tile, int hi) {
+    hi = max(hi, 0);
+    if (wave == 0) dma4(row_tab + min(max(tile * BN - BN / 2 + key_k, 0), hi), SlK[tile & 3]);
+    else if (wave == 1) dma4(row_tab + min(tile * BN + key_v, hi), SlV[tile & 3]);
   };
 
   // The softmax runs on 32-key halves of a tile ("half tiles", numbered u =
@@ -441,9 +474,13 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void extend_bf16(ExtendArgs a) {
     constexpr int WPS = 4 * QB / NK;        // exponential words per X stage
     constexpr int NG = 2 * NDMA;            // gathers of this block (K and V alternating)
     static_assert(WPS * NK == 4 * QB, "exponential words split evenly over X");
-    // slots of this block's gathers (contiguous per lane)
-    const int32_t* kslots = SlK[gk & 3] + (wave * RPI + drow) * NDMA;
-    const int32_t* vslots = SlV[(gk - 1) & 3] + (wave * RPI + drow) * NDMA;
+    // slots of this block's gathers, read before its first operands (the
+    // first stage's wait then covers them)
+    slotv ksl, vsl;
+    if constexpr (GATHER) {
+      ksl = lane_slots(SlK[gk & 3]);
+      vsl = lane_slots(SlV[(gk - 1) & 3]);
+    }
     bf16x8 kop[NK];
     if constexpr (QK) {
       kop[0] = k_op(ks, hk, 0);
@@ -469,7 +506,7 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void extend_bf16(ExtendArgs a) {
           const int j = gi >> 1;
           // out-of-range slots are clamped into the pool (the debug check
           // runs beside the kernel)
-          const uint32_t slot = min((uint32_t)((gi & 1) ? vslots[gi >> 1] : kslots[gi >> 1]), P - 1);
+          const uint32_t slot = min((uint32_t)((gi & 1) ? vsl[gi >> 1] : ksl[gi >> 1]), P - 1);
           const int R = dma_row(wave, j, drow);
           if (gi & 1)
             dma16(vg + (uint64_t)slot * slot_bytes + (dch ^ swz_v<CH>(R)) * 16, vdst + (wave * NDMA + j) * 1024);
@@ -515,12 +552,38 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void extend_bf16(ExtendArgs a) {
   f32x4 s_ev[QB][2], s_od[QB][2];
 
   // prologue: slots of tiles 0..2; K tiles 0 and 1 (keys -32..95), V tile 0;
-  // QK of half tile 0 (the second half of K tile 0) and its maxima
-  dma_slots(0);
-  dma_slots(1);
-  dma_slots(2);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  // QK of half tile 0 (the second half of K tile 0) and its maxima.  With
+  // uniform new-token counts the prefix length is still in flight: the slot
+  // indices are read up to the end of the table row, and read again with
+  // the request's own bound if it ends inside these three tiles (so that no
+  // row outside the request is gathered).
+  {
+    const int hi0 = uni ? (int)min(a.ld, (int64_t)0x7fffffff) - 1 : kv_end - 1;
+    if (uni) p = a.prefix_lens[r];
+    dma_slots(0, hi0);
+    dma_slots(1, hi0);
+    dma_slots(2, hi0);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (uni) {
+      set_bounds();
+      if (kv_end < min(3 * BN, hi0 + 1)) {
+        dma_slots(0, kv_end - 1);
+        dma_slots(1, kv_end - 1);
+        dma_slots(2, kv_end - 1);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
+    }
+  }
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    qvalid[qb] = qvalid[qb] && p + qj[qb] < kv_end;
+    // last visible key, relative to the first key this lane holds in a
+    // 32-key half tile
+    qlim[qb] = (qvalid[qb] ? p + qj[qb] : kv_end - 1) - 8 * gq;
+  }
   dma_k(0, I0{});
   dma_v(0, I0{});
   dma_k(1, I1{});
@@ -565,7 +628,7 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void extend_bf16(ExtendArgs a) {
     // gathers read them), so no register has to wait for them.  Past the
     // last tile the keys are clamped: the gathers then refill the stage
     // consumed in the previous iteration with rows nobody reads again.
-    dma_slots(tile + 3);
+    dma_slots(tile + 3, kv_end - 1);
     char* kn = kbuf(NPAR{});      // K tile t+1
     char* kd = kbuf(par);         // K tile t+2 lands in the stage K tile t used
     char* vs = vbuf(par);         // V tile t
@@ -733,6 +796,10 @@ extern "C" int rkv_attn_extend(const void* q, const void* k_pool, const void* v_
     const int64_t per_req = ((int64_t)max_new * a.G + BM - 1) / BM;
     const int64_t ragged = (total_new * a.G + BM - 1) / BM + B;
     a.tiles_bound = per_req * B < ragged ? per_req * B : ragged;
+    // with total_new == B * max_new and every n_r <= max_new, every request
+    // has max_new new tokens
+    a.uni_n = total_new == (int64_t)B * max_new ? max_new : 0;
+    a.tiles_per_req = per_req;
     int64_t grid = a.tiles_bound * hkv;
     grid = (grid + rkv::kXcds - 1) / rkv::kXcds * rkv::kXcds;
     if (grid > 0x7fffffff) return rkv::fail(RKV_ENOTSUP, "rkv_attn_extend: grid too large");
@@ -743,6 +810,8 @@ extern "C" int rkv_attn_extend(const void* q, const void* k_pool, const void* v_
       hipLaunchKernelGGL(extend_bf16<64>, dim3((unsigned)grid), dim3(NWAVES * 64), 0, st, a);
   } else {
     a.tiles_bound = 0;
+    a.uni_n = 0;
+    a.tiles_per_req = 0;
     const int64_t waves = total_new * hq;
     const int64_t grid = (waves + 3) / 4;
     if (grid > 0x7fffffff) return rkv::fail(RKV_ENOTSUP, "rkv_attn_extend: grid too large");

@@ -34,7 +34,7 @@ class Batch:
     max_len: int
     total_new: int
     uploaded: object = None     # event after the tables' upload (the host tables are its source)
-    order: torch.Tensor = None  # device int32 [B]: longest requests first, extend's work order
+    order: torch.Tensor = None  # device int32 [B]: extend's work order (longest first); None = batch order
 
 
 class RadixKVCache:
@@ -74,13 +74,17 @@ class RadixKVCache:
         code, tb = self.tree.batch_prepare(seqs, ld, out=h[:lay[-1]])
         if code != rkv.OK:
             raise rkv.RkvError(code, "batch_prepare: eviction cannot free enough slots")
-        h[ow:ow + B] = self.extend_order(tb["seq_lens"])
+        order = self.extend_order(tb["seq_lens"])
+        h[ow:ow + B] = order
         dev = pinned.to(self.device, non_blocking=True)
         uploaded = torch.cuda.Event()
         uploaded.record()
         T = int(tb["qo_indptr"][B])
         n = tb["seq_lens"].astype(np.int64) - tb["prefix_lens"]
-        return Batch(seqs=seqs, host=tb, order=dev[ow:ow + B], req_to_token=dev[:lay[1]].view(-1, ld)[:B],
+        # batch order needs no order array (and spares extend one load)
+        in_order = bool(np.array_equal(order, np.arange(B)))
+        return Batch(seqs=seqs, host=tb, order=None if in_order else dev[ow:ow + B],
+                     req_to_token=dev[:lay[1]].view(-1, ld)[:B],
                      prefix_lens=dev[lay[1]:lay[1] + B], seq_lens=dev[lay[2]:lay[2] + B],
                      qo_indptr=dev[lay[3]:lay[3] + B + 1], new_slots=dev[lay[4]:lay[4] + T],
                      max_new=int(n.max()) if len(n) else 0,
