@@ -80,6 +80,7 @@ struct ExtendArgs {
   int64_t total_new;        // q rows; rows at or past it are never read
   int32_t uni_n;            // > 0: every request has this many new tokens
   int64_t tiles_per_req;    // work items per request when uni_n > 0
+  uint32_t g_magic;         // ceil(2^32 / G) for G > 1: x / G = mulhi(x, g_magic) for x < 2^28
   int* err;
 };
 
@@ -223,9 +224,12 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void extend_bf16(ExtendArgs a) {
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
 
-  const int64_t w = rkv::xcd_work_item(blockIdx.x, gridDim.x);
-  const int g = (int)(w / a.tiles_bound);
-  const int64_t tg = w % a.tiles_bound;
+  // item decode in 32 bits (the grid is below 2^31): a 64-bit division by a
+  // run-time value costs hundreds of instructions
+  const uint32_t w = (uint32_t)rkv::xcd_work_item(blockIdx.x, gridDim.x);
+  const uint32_t tb = (uint32_t)a.tiles_bound;
+  const int g = (int)(w / tb);
+  const int64_t tg = w - (uint32_t)g * tb;
   if (g >= a.hkv) return;
   int r = 0, t = 0, q0 = 0, n = 0, p = 0;
   const bool uni = a.uni_n > 0;
@@ -234,9 +238,10 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void extend_bf16(ExtendArgs a) {
     // the request and tile follow from the work item's index, and the
     // prefix length is loaded beside the first slot indices and queries
     // below instead of before them (one dependent memory round trip less)
-    const int64_t i = tg / a.tiles_per_req;
-    if (i >= a.B) return;
-    t = (int)(tg - i * a.tiles_per_req);
+    const uint32_t tpr = (uint32_t)a.tiles_per_req;
+    const uint32_t i = (uint32_t)tg / tpr;
+    if (i >= (uint32_t)a.B) return;
+    t = (int)((uint32_t)tg - i * tpr);
     r = (int)i;
     if (a.order) {
       r = a.order[i];
@@ -254,6 +259,8 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void extend_bf16(ExtendArgs a) {
   const int l16 = lane & 15;
   const int gq = lane >> 4;
   const int G = a.G;
+  // row / G for the non-negative row numbers of a request (below 2^28)
+  auto div_g = [&](int x) -> int { return G == 1 ? x : (int)__umulhi((uint32_t)x, a.g_magic); };
   const int rows_total = n * G;
   const int row0 = t * BM;
   const int row_last = min(row0 + BM, rows_total) - 1;
@@ -269,7 +276,7 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void extend_bf16(ExtendArgs a) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = row0 + wave * (QB * 16) + qb * 16 + l16;
-    const int j = row / G;
+    const int j = div_g(row);
     qvalid[qb] = row < rows_total && (int64_t)q0 + j < a.total_new;
     qj[qb] = qvalid[qb] ? j : 0;
     const int hh = qvalid[qb] ? row - j * G : 0;
@@ -301,10 +308,10 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void extend_bf16(ExtendArgs a) {
   // bounds that follow from the prefix length are set once it has arrived
   int kv_end = 0, ntiles = 0, first_mask_tile = 0;
   auto set_bounds = [&]() {
-    kv_end = (int)min((int64_t)p + row_last / G + 1, a.ld);
+    kv_end = (int)min((int64_t)p + div_g(row_last) + 1, a.ld);
     ntiles = (kv_end + BN - 1) / BN;
     // tiles before this one are fully visible to every row of the workgroup
-    first_mask_tile = min(ntiles, (p + row0 / G) / BN);
+    first_mask_tile = min(ntiles, (p + div_g(row0)) / BN);
   };
   if (!uni) set_bounds();
 
@@ -342,16 +349,6 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void extend_bf16(ExtendArgs a) {
     const int R = dma_row(wave, j, drow);
     const int lch = dch ^ (decltype(is_k)::value ? swz_k<CH>(R) : swz_v<CH>(R));
     dma16(src + (uint64_t)slot * slot_bytes + lch * 16, dst + (wave * NDMA + j) * 1024);
-  };
-  auto dma_k = [&](int tile, auto par) {
-    const slotv sl = lane_slots(SlK[tile & 3]);
-#pragma unroll
-    for (int j = 0; j < NDMA; ++j) gather1(sl[j], kbuf(par), kg, j, std::true_type{});
-  };
-  auto dma_v = [&](int tile, auto par) {
-    const slotv sl = lane_slots(SlV[tile & 3]);
-#pragma unroll
-    for (int j = 0; j < NDMA; ++j) gather1(sl[j], vbuf(par), vg, j, std::false_type{});
   };
   // slot indices of tile `tile` into stage tile & 3 (wave 0 for K, wave 1
   // for V, one 4-byte DMA each, straight from the table; keys clamped into
@@ -584,9 +581,16 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void extend_bf16(ExtendArgs a) {
     // 32-key half tile
     qlim[qb] = (qvalid[qb] ? p + qj[qb] : kv_end - 1) - 8 * gq;
   }
-  dma_k(0, I0{});
-  dma_v(0, I0{});
-  dma_k(1, I1{});
+  {
+    // the three tiles' slots first, so their LDS reads overlap
+    const slotv sk0 = lane_slots(SlK[0]), sv0 = lane_slots(SlV[0]), sk1 = lane_slots(SlK[1]);
+#pragma unroll
+    for (int j = 0; j < NDMA; ++j) gather1(sk0[j], K0, kg, j, std::true_type{});
+#pragma unroll
+    for (int j = 0; j < NDMA; ++j) gather1(sv0[j], V0, vg, j, std::false_type{});
+#pragma unroll
+    for (int j = 0; j < NDMA; ++j) gather1(sk1[j], K1, kg, j, std::true_type{});
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 #pragma unroll
@@ -605,7 +609,16 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void extend_bf16(ExtendArgs a) {
                                             : lane_max(s_ev, qb, 0, std::false_type{});
       raise0 |= row_max(lm, qb);
     }
-    if (__builtin_amdgcn_ballot_w64(raise0)) rescale(mt);
+    // first half tile: O and the row sums are still zero, so only the
+    // reference and the threshold are set
+    if (__builtin_amdgcn_ballot_w64(raise0)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float rmx = rkv::max_xor32(rkv::max_xor16(mt[qb]));
+        mref[qb] = rmx * c;
+        thr[qb] = (mref[qb] + kRescaleThreshold) / c;
+      }
+    }
   }
 
   // iteration t (half tile 2t's maxima taken; K tile t+1 = half tiles 2t+1
@@ -776,6 +789,8 @@ extern "C" int rkv_attn_extend(const void* q, const void* k_pool, const void* v_
   if (dtype != RKV_F32 && dtype != RKV_BF16) return rkv::fail(RKV_ENOTSUP, "rkv_attn_extend: dtype");
   if (d != 64 && d != 128) return rkv::fail(RKV_ENOTSUP, "rkv_attn_extend: head_dim must be 64 or 128");
   if (hq % hkv != 0 || hq / hkv > 16) return rkv::fail(RKV_ENOTSUP, "rkv_attn_extend: Hq/Hkv must be an integer <= 16");
+  if ((int64_t)max_new * (hq / hkv) >= ((int64_t)1 << 28))
+    return rkv::fail(RKV_ENOTSUP, "rkv_attn_extend: max_new * Hq/Hkv must be below 2^28");
   if (B == 0 || total_new == 0) return RKV_OK;
   if (!q || !k_pool || !v_pool || !o || !req_to_token || !qo_indptr || !prefix_lens)
     return rkv::fail(RKV_EINVAL, "rkv_attn_extend: NULL pointer");
@@ -800,6 +815,7 @@ extern "C" int rkv_attn_extend(const void* q, const void* k_pool, const void* v_
     // has max_new new tokens
     a.uni_n = total_new == (int64_t)B * max_new ? max_new : 0;
     a.tiles_per_req = per_req;
+    a.g_magic = a.G > 1 ? (uint32_t)((((uint64_t)1 << 32) + a.G - 1) / a.G) : 0u;
     int64_t grid = a.tiles_bound * hkv;
     grid = (grid + rkv::kXcds - 1) / rkv::kXcds * rkv::kXcds;
     if (grid > 0x7fffffff) return rkv::fail(RKV_ENOTSUP, "rkv_attn_extend: grid too large");
@@ -812,6 +828,7 @@ extern "C" int rkv_attn_extend(const void* q, const void* k_pool, const void* v_
     a.tiles_bound = 0;
     a.uni_n = 0;
     a.tiles_per_req = 0;
+    a.g_magic = 0;
     const int64_t waves = total_new * hq;
     const int64_t grid = (waves + 3) / 4;
     if (grid > 0x7fffffff) return rkv::fail(RKV_ENOTSUP, "rkv_attn_extend: grid too large");
