@@ -259,8 +259,12 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void extend_bf16(ExtendArgs a) {
   const int l16 = lane & 15;
   const int gq = lane >> 4;
   const int G = a.G;
-  // row / G for the non-negative row numbers of a request (below 2^28)
-  auto div_g = [&](int x) -> int { return G == 1 ? x : (int)__umulhi((uint32_t)x, a.g_magic); };
+  // row / G for the non-negative row numbers of a request (below 2^28); the
+  // high half of the product is written out (the library's __umulhi is a
+  // call that is not inlined here)
+  auto div_g = [&](int x) -> int {
+    return G == 1 ? x : (int)(((uint64_t)(uint32_t)x * a.g_magic) >> 32);
+  };
   const int rows_total = n * G;
   const int row0 = t * BM;
   const int row_last = min(row0 + BM, rows_total) - 1;
