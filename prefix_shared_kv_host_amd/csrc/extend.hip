@@ -678,22 +678,41 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void extend_bf16(ExtendArgs a) {
     }
   }
 
-  // ---- epilogue: lane holds o[query l16][d = db*16 + 4*gq + 0..3]
+  // ---- epilogue: lane holds o[query l16][d = db*16 + 4*gq + 0..3].  The
+  //      normalized rows go through this wave's 32 rows of LDS (the K stages
+  //      are free after the loop's last barrier: no read of them and no copy
+  //      into them is outstanding), so that each store instruction writes
+  //      whole rows of D bf16 instead of 32-byte pieces of 16 rows.
+  static_assert(2 * 32 * ROWB <= TILEB, "two waves' rows fit one K stage");
+  char* stage = (wave < 2 ? K0 : K1) + (wave & 1) * (32 * ROWB);
   uint16_t* obase = (uint16_t*)a.o;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float lsum = lacc[qb][0];
-    if (!qvalid[qb]) continue;
     const float inv = 1.f / lsum;
-    uint16_t* orow = obase + ((int64_t)qtok[qb] * a.hq + qhead[qb]) * D;
+    const int r = qb * 16 + l16;
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) {
       const f32x4 v = oacc[qb][db];
-      *(uint2*)(orow + db * 16 + 4 * gq) =
+      const int c16 = db * 2 + (gq >> 1);
+      *(uint2*)(stage + r * ROWB + ((c16 ^ (r & (CH - 1))) << 4) + (gq & 1) * 8) =
           make_uint2(rkv::pack_bf16x2(v[0] * inv, v[1] * inv), rkv::pack_bf16x2(v[2] * inv, v[3] * inv));
     }
-    if (a.lse && gq == 0)
+    if (qvalid[qb] && a.lse && gq == 0)
       a.lse[(int64_t)qtok[qb] * a.hq + qhead[qb]] = (mref[qb] + log2f(lsum)) * 0.69314718055994531f;
+  }
+  {
+    constexpr int RPS = 64 / CH;            // rows per store instruction
+    const int c = lane % CH;
+#pragma unroll
+    for (int k = 0; k < 32 / RPS; ++k) {
+      const int r = k * RPS + lane / CH;
+      const uint4 val = *(const uint4*)(stage + r * ROWB + ((c ^ (r & (CH - 1))) << 4));
+      const int row = row0 + wave * 32 + r;
+      const int j = div_g(row);
+      if (row < rows_total && (int64_t)q0 + j < a.total_new && p + j < kv_end)
+        *(uint4*)(obase + ((int64_t)(q0 + j) * a.hq + g * G + (row - j * G)) * D + c * 8) = val;
+    }
   }
 }
 
