@@ -174,10 +174,30 @@ class RadixKVCache:
             self._ws = torch.empty(max((need + 3) // 4, 1), dtype=torch.float32, device=self.device)
         return self._ws
 
-    def decode(self, batch: Batch, q, o=None, lse=None, num_splits=0, stream=None):
+    def decode_splits(self, batch: Batch, hq):
+        """Splits per request for plain decode: 0 (768-key chunks, so a
+        request's output bits do not depend on its batch) unless the
+        grouped-head kernel (bf16, Hq/Hkv >= 4) would then get fewer items
+        than MIN_TAIL_ITEMS; then enough splits for that many items, with
+        chunks of at least 256 keys.  Such launches are latency-bound and
+        shorter items finish sooner (one GPU's 8/1 heads of the 64/8-head
+        decode batch: 33.1 -> 30.9 us at 16 splits)."""
+        L = batch.host["seq_lens"].astype(np.int64)
+        if hq // self.hkv < 4 or self.k_pool.dtype != torch.bfloat16 or len(L) == 0:
+            return 0
+        if int(((L + 767) // 768).sum()) * self.hkv >= self.MIN_TAIL_ITEMS:
+            return 0
+        ns = -(-self.MIN_TAIL_ITEMS // (len(L) * self.hkv))
+        ns = min(ns, int(L.max()) // 256)
+        return ns if ns > -(-int(L.max()) // 768) else 0
+
+    def decode(self, batch: Batch, q, o=None, lse=None, num_splits=None, stream=None):
+        """Plain decode; num_splits None: the rule of decode_splits."""
         if o is None:
             o = torch.empty_like(q)
         B, hq, _ = q.shape
+        if num_splits is None:
+            num_splits = self.decode_splits(batch, hq)
         ws = self.workspace(B, hq, batch.max_len, num_splits)
         rkv.attn_decode(q, self.k_pool, self.v_pool, o, batch.req_to_token, batch.seq_lens,
                         batch.max_len, ws, lse=lse, num_splits=num_splits, stream=stream)

@@ -68,7 +68,7 @@ def needed_slots(shape, phases, select):
 ORACLE_CHUNK = 8   # requests per oracle call, each followed by a progress line
 
 
-def run(shape, phases, select=lambda i, B: None, num_splits=0, content_device="cuda",
+def run(shape, phases, select=lambda i, B: None, num_splits=None, content_device="cuda",
         with_lse=True, sparse=False, cascade=None, phase_source=None):
     """Returns a list of per-checked-phase dicts with GPU and oracle outputs
     restricted to the selected requests' rows.  cascade: None for plain

@@ -41,3 +41,36 @@ def test_dealt_over_xcds_otherwise(B):
             assert np.all(np.diff(b) < 0)                          # longest first within it
         sums = [int(b.sum()) for b in bins]
         assert max(sums) - min(sums) <= B                          # the snake keeps the bins even
+
+
+class _Pool:
+    def __init__(self, dtype):
+        self.dtype = dtype
+
+
+def splits_for(hq, hkv, lens, dtype="bf16"):
+    import torch
+    from types import SimpleNamespace
+    c = RadixKVCache.__new__(RadixKVCache)
+    c.hkv = hkv
+    c.k_pool = _Pool(torch.bfloat16 if dtype == "bf16" else torch.float32)
+    b = SimpleNamespace(host={"seq_lens": np.asarray(lens, dtype=np.int32)})
+    return c.decode_splits(b, hq)
+
+
+def test_plain_decode_splits_rule():
+    """Plain decode keeps 768-key chunks (num_splits 0) unless the grouped-head
+    kernel would get fewer than 1024 items; then enough splits for 1024 items,
+    never chunks below 256 keys, and only when that is more splits than the
+    longest request already has."""
+    rng = np.random.default_rng(7)
+    long_ = rng.integers(2049, 8193, 64)
+    assert splits_for(64, 8, long_) == 0             # 64 x 8 heads: thousands of items already
+    assert splits_for(8, 1, long_) == 16             # one GPU's 8/1-head share: 16 splits -> 1024 items
+    assert splits_for(32, 32, long_) == 0            # multi-head: the vector kernel
+    assert splits_for(8, 1, long_, "f32") == 0       # fp32: the vector kernel
+    assert splits_for(8, 1, [300] * 4) == 0          # 256-key chunks would give 2 splits, no more than 768's 1
+    assert splits_for(8, 1, [4096] * 4) == 16        # 4 x 16 = 64 items, capped by 4096 / 256 = 16
+    ns = splits_for(8, 1, [2000] * 8)
+    assert ns == 2000 // 256 and ns > -(-2000 // 768)
+    assert splits_for(8, 1, []) == 0
