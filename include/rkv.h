@@ -367,8 +367,9 @@ size_t rkv_attn_decode_workspace_bytes(int32_t B, int32_t hq, int32_t d, int32_t
  * and attends to all L_r keys req_to_token[r, 0..L_r) (same formula as
  * extend).  Split-KV: the keys of a request are cut into S_r contiguous
  * chunks, each reduced to a partial (max, sum, acc) in fp32, then merged by
- * log-sum-exp rescaling.  S_r depends only on L_r and num_splits (0 = a
- * fixed chunk of 768 keys; N > 0 = at most N chunks), never on the rest of
+ * log-sum-exp rescaling.  S_r depends only on L_r and num_splits (0 =
+ * ceil(L_r / 768) chunks of equal length, rounded up to 64 keys; N > 0 = at
+ * most N chunks), never on the rest of
  * the batch, so a request's output bits do not depend on its batch.  Every
  * seq_lens[r] must be <= max_seq_len and <= ld.  `workspace` (ws_bytes >=
  * rkv_attn_decode_workspace_bytes) holds the partials.

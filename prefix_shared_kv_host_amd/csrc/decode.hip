@@ -103,10 +103,17 @@ __device__ __forceinline__ uint4 load_kv(const char* p) {
   }
 }
 
+// Keys per split of a request of L keys.  num_splits > 0: at most that many
+// splits.  0: ceil(L / kChunk) splits, the count of kChunk-key chunks, but
+// of equal length (rounded up to 64 keys, so never above kChunk, and the
+// count stays the same): a short last split per request would leave the
+// launch's last round to full-length items.  Either way the split depends
+// only on L.
 __host__ __device__ inline int split_chunk(int L, int num_splits) {
-  if (num_splits <= 0) return kChunk;
-  int c = (L + num_splits - 1) / num_splits;
-  return ((c + 63) / 64) * 64;
+  int n = num_splits > 0 ? num_splits : (L + kChunk - 1) / kChunk;
+  if (n < 1) n = 1;
+  const int c = (L + n - 1) / n;
+  return c < 64 ? 64 : ((c + 63) / 64) * 64;
 }
 
 // Keys [k_begin, k_end) of split s of request r (of length L), and where its
@@ -134,8 +141,11 @@ __device__ __forceinline__ bool split_span(const DecodeArgs& a, int r, int s, in
     return false;
   }
   if (s >= nsplit) return false;
-  k_begin = tb + s * a.tail_chunk;
-  k_end = min(L, k_begin + a.tail_chunk);
+  // the tail's nsplit splits of equal length (rounded up to 64 keys, never
+  // above tail_chunk: every split keeps at least one key)
+  const int tc = min(a.tail_chunk, ((L - tb + nsplit - 1) / nsplit + 63) / 64 * 64);
+  k_begin = tb + s * tc;
+  k_end = min(L, k_begin + tc);
   rec = (r1 - r0 == 1) ? -1 : r1 - nsplit + s;
   if (rec >= 0 && !a.ws) {
     if (a.err) rkv::raise_flag(a.err);
