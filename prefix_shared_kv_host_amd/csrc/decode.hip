@@ -589,6 +589,20 @@ __device__ __forceinline__ void shared_item(const DecodeArgs& a, const SharedJob
   }
 }
 
+// Block b of a prefix-shared launch on the matrix cores of `total` blocks,
+// `sb` of them shared (both multiples of 8): whether it runs a shared item,
+// and its index among the blocks of its kind.  The kinds are interleaved in groups of 8
+// consecutive blocks (one per XCD) in proportion to their counts, so the
+// latency-bound shared items run beside the bandwidth-bound tails instead of
+// all before them; group g of a kind holds that kind's blocks 8g .. 8g+7, so
+// each kind keeps its XCD-contiguous item ranges.
+__device__ __forceinline__ bool cascade_block(int64_t b, int64_t sb, int64_t total, int64_t& idx) {
+  const int64_t gt = total / rkv::kXcds, gs = sb / rkv::kXcds, g = b / rkv::kXcds;
+  const int64_t c0 = g * gs / gt, c1 = (g + 1) * gs / gt;   // shared groups before g, and through g
+  idx = (c1 > c0 ? c0 : g - c0) * rkv::kXcds + b % rkv::kXcds;
+  return c1 > c0;
+}
+
 // Phase 1.  Work item = (request, split, block of HB kv heads [, q-head
 // group]).  A key's rows for the HB heads are HB*D contiguous elements of the
 // slot, so the workgroup reads them as one contiguous run: lane group
@@ -616,6 +630,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CB > 0 ? 2 
     // the two V stages of each wave, as two arrays (see walk)
     __shared__ __attribute__((aligned(16))) char V0[4][32 * D * 2];
     __shared__ __attribute__((aligned(16))) char V1[4][32 * D * 2];
+    // shared blocks first: interleaved with the tails (as the matrix-core
+    // kernel does) the 32-head batch ran 2 % slower, its shared runs no
+    // longer read side by side from L2
     const int b = (int)blockIdx.x;
     if (b < shared_blocks) {
       const int wave = (int)(threadIdx.x >> 6);
@@ -825,13 +842,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   __shared__ __attribute__((aligned(16))) char V0[32 * D * 2];
   __shared__ __attribute__((aligned(16))) char V1[32 * D * 2];
   __shared__ __attribute__((aligned(16))) char KS[32 * D * 2];
-  const int b = (int)blockIdx.x;
-  if (b < shared_blocks) {
-    const int64_t w = rkv::xcd_work_item(b, shared_blocks);
+  int64_t idx;
+  if (cascade_block(blockIdx.x, shared_blocks, gridDim.x, idx)) {
+    const int64_t w = rkv::xcd_work_item(idx, shared_blocks);
     if (w < (int64_t)j.n_jobs * a.hkv) shared_item<D, CB, true>(a, j, w, V0, V1, KS);
     return;
   }
-  gqa_item<D, TAIL_STREAM>(a, rkv::xcd_work_item(b - shared_blocks, (int64_t)gridDim.x - shared_blocks), V0, V1, KS);
+  gqa_item<D, TAIL_STREAM>(a, rkv::xcd_work_item(idx, (int64_t)gridDim.x - shared_blocks), V0, V1, KS);
 }
 
 // Phase 2: one wave per (request, q head); lanes cover D.
