@@ -21,7 +21,8 @@
 //            log-sum-exp rescaling.
 //
 // S_r depends only on L_r (and the caller's num_splits), never on the rest of
-// the batch, so a request's output bits do not depend on its batch.
+// the batch, so a request's output bits do not depend on its batch; by
+// default a request gets ceil(L_r / 768) splits of equal length.
 
 #include <hip/hip_runtime.h>
 #include <math.h>

@@ -39,6 +39,10 @@
 //   * fp32 online softmax in the log2 domain (exp2 with log2(e) folded into
 //     the scale); weights rounded to bf16 for PV; o rounded to bf16 (RNE).
 //   * causal masking only on tiles that reach past a workgroup's first query.
+//   * when every request has the same number of new tokens, a work item's
+//     request follows from its index and the prefix length is loaded beside
+//     the first slot indices (one dependent round trip less); the output
+//     rows leave through LDS as whole rows.
 // fp32 path: one wave per (query row, head), fp32 FMA throughout.
 
 #include <hip/hip_runtime.h>
