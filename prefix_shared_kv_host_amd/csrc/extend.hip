@@ -274,9 +274,10 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void extend_bf16(ExtendArgs a) {
   const int row_last = min(row0 + BM, rows_total) - 1;
 
   // ---- queries of this wave: rows row0 + wave*32 + qb*16 + l16.  Every
-  //      lane loads a query (a row past the request's rows reads q row 0,
-  //      and a row whose position lies past the table row its own), so the
-  //      loads need no branch; only valid rows are written.
+  //      lane loads a query, so the loads need no branch: a row past the
+  //      request's rows reads q row 0, and a row whose key position lies
+  //      past the table row still reads its own.  Only valid rows are
+  //      written.
   bf16x8 qreg[QB][KSTEPS];
   int qlim[QB], qhead[QB], qtok[QB], qj[QB];
   bool qvalid[QB];

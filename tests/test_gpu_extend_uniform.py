@@ -29,6 +29,8 @@ CASES = [
     (52, 8, 2, 128, 300, 129),    # several row tiles per request; one short request
     (53, 4, 1, 64, 190, 1),       # one query row per request, keys end at 191
     (54, 32, 32, 128, 1024, 16),  # multi-head, one key tile past the prefix
+    (55, 4, 1, 128, 128, 64),     # keys end exactly at the third tile's end (192)
+    (56, 4, 1, 128, 127, 64),     # one key short of it (191): the slots are read again
 ]
 
 
