@@ -49,3 +49,17 @@ def test_host_argument_errors():
     # B * Hq * splits(1024 keys / 256 per split) * (D + 4) floats
     assert L.rkv_attn_decode_workspace_bytes(4, 8, 128, 1024, 0) == 4 * 8 * 2 * 132 * 4   # 768-key chunks
     assert L.rkv_attn_decode_workspace_bytes(4, 8, 128, 1024, 3) == 4 * 8 * 3 * 132 * 4
+
+
+def test_extend_rejects_rows_beyond_the_division_bound():
+    """rkv_attn_extend divides row numbers by Hq/Hkv with a multiply-high,
+    exact below 2^28 rows per request: larger batches are refused on the
+    host, before any device call (dummy pointers are never touched)."""
+    L = rkv.lib()
+    p = 16  # any non-null value: the call returns before dereferencing
+    args = lambda max_new, hq, hkv: (p, p, p, p, None, p, 4096, p, p, None, 2, 2 * max_new, max_new,
+                                     hq, hkv, 128, 0.088, rkv.BF16, 1 << 20, None)
+    assert L.rkv_attn_extend(*args(1 << 25, 8, 1)) == rkv.ENOTSUP      # 2^25 tokens x 8 heads = 2^28 rows
+    assert L.rkv_attn_extend(*args(1 << 28, 1, 1)) == rkv.ENOTSUP
+    assert L.rkv_attn_extend(*args(1 << 27, 3, 1)) == rkv.ENOTSUP      # 3 * 2^27 >= 2^28
+    assert L.rkv_attn_extend(*args(1 << 24, 17, 1)) == rkv.ENOTSUP     # Hq/Hkv above 16
