@@ -591,12 +591,13 @@ __device__ __forceinline__ void shared_item(const DecodeArgs& a, const SharedJob
 }
 
 // Block b of a prefix-shared launch on the matrix cores of `total` blocks,
-// `sb` of them shared (both multiples of 8): whether it runs a shared item,
-// and its index among the blocks of its kind.  The kinds are interleaved in groups of 8
-// consecutive blocks (one per XCD) in proportion to their counts, so the
-// latency-bound shared items run beside the bandwidth-bound tails instead of
-// all before them; group g of a kind holds that kind's blocks 8g .. 8g+7, so
-// each kind keeps its XCD-contiguous item ranges.
+// `sb` of them shared (both multiples of 8, total > 0): whether it runs a
+// shared item, and its index among the blocks of its kind.  The kinds are
+// interleaved in groups of 8 consecutive blocks (one per XCD) in proportion
+// to their counts, so the latency-bound shared items run beside the
+// bandwidth-bound tails instead of all before them; group g of a kind holds
+// that kind's blocks 8g .. 8g+7, so each kind keeps its XCD-contiguous item
+// ranges.
 __device__ __forceinline__ bool cascade_block(int64_t b, int64_t sb, int64_t total, int64_t& idx) {
   const int64_t gt = total / rkv::kXcds, gs = sb / rkv::kXcds, g = b / rkv::kXcds;
   const int64_t c0 = g * gs / gt, c1 = (g + 1) * gs / gt;   // shared groups before g, and through g
