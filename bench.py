@@ -161,7 +161,8 @@ def gqa_halves(steps, warmup, cfg=None):
     """Llama-70B-shaped GQA (c4: 64 q / 8 kv heads, D=128, bf16, a shared
     2048-token prefix): the extend half (64 requests x 256 new tokens) and the
     decode half (64 requests x 1 token), each kv_scatter + attention, timed
-    with HIP events on the launch stream; reported separately and summed.
+    with HIP events on the launch stream over calls issued back to back (and,
+    as us_synced, one call at a time); reported separately and summed.
     cfg: another config with c4's phases (its heads may differ)."""
     import torch
     from inputs import configs
@@ -181,13 +182,16 @@ def gqa_halves(steps, warmup, cfg=None):
             torch.cuda.synchronize()
             sc.append(ev[0].elapsed_time(ev[1])); at.append(ev[1].elapsed_time(ev[2]))
         tb, s_ = ph.batch.host, ph.shape
-        us, sus = float(np.mean(at)) * 1e3, float(np.mean(sc)) * 1e3
+        # us: issued back to back, as in the step loop; us_synced: one call
+        # at a time, synchronized after each (adds the launch latency)
+        sus, us = back_to_back_us([ph.scatter, ph.attend], steps)
+        synced = dict(us_synced=float(np.mean(at)) * 1e3, scatter_us_synced=float(np.mean(sc)) * 1e3)
         T = int(tb["qo_indptr"][-1])
         if name == "extend":
             F = extend_flops(tb["prefix_lens"], tb["seq_lens"], s_.hq, s_.d)
             out[name] = dict(kernel="attn_extend", us=us, scatter_us=sus, flop=F, tflops=F / (us * 1e-6) / 1e12,
                              frac_of_peak=F / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
-                             tokens_per_s=T / ((us + sus) * 1e-6))
+                             tokens_per_s=T / ((us + sus) * 1e-6), **synced)
         else:
             Bl = decode_bytes(tb["seq_lens"], s_.hq, s_.hkv, s_.d, 2)
             uniq = len(np.unique(np.concatenate([tb["req_to_token"][r][: tb["seq_lens"][r]]
@@ -196,7 +200,7 @@ def gqa_halves(steps, warmup, cfg=None):
             out[name] = dict(kernel="attn_decode", us=us, scatter_us=sus, bytes_logical=Bl, bytes_unique=Bu,
                              logical_equiv_gbs=Bl / (us * 1e-6) / 1e9, gbs_unique=Bu / (us * 1e-6) / 1e9,
                              frac_of_peak_unique=Bu / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
-                             tokens_per_s=T / ((us + sus) * 1e-6))
+                             tokens_per_s=T / ((us + sus) * 1e-6), **synced)
             # the same batch through the prefix-shared path (64 requests under
             # one 2048-token prefix)
             ph.use_cascade()
@@ -207,11 +211,13 @@ def gqa_halves(steps, warmup, cfg=None):
                 ev[1].record(stream); ph.attend(); ev[2].record(stream)
                 torch.cuda.synchronize()
                 cas.append(ev[1].elapsed_time(ev[2]))
-            cus = float(np.mean(cas)) * 1e3
-            out[name]["cascade"] = dict(kernel="attn_decode_cascade", us=cus, bytes_plan=ph.plan_bytes(),
+            (cus,) = back_to_back_us([ph.attend], steps)
+            out[name]["cascade"] = dict(kernel="attn_decode_cascade", us=cus, us_synced=float(np.mean(cas)) * 1e3,
+                                        bytes_plan=ph.plan_bytes(),
                                         gbs_plan=ph.plan_bytes() / (cus * 1e-6) / 1e9,
                                         frac_of_peak=ph.plan_bytes() / (cus * 1e-6) / 1e9 / PEAK_HBM_GBS,
-                                        jobs=ph.plan.n_jobs, host_plan_ms=ph.plan_ms)
+                                        jobs=ph.plan.n_jobs, seg_chunk=ph.plan.seg_chunk,
+                                        tail_chunk=ph.plan.tail_chunk, host_plan_ms=ph.plan_ms)
             # both decode paths captured into a HIP graph and replayed: the
             # same kernels without the host side of each call
             out[name]["graph_us"] = graph_replay_us(ph.attend_plain, steps, warmup)
@@ -223,6 +229,28 @@ def gqa_halves(steps, warmup, cfg=None):
     out["workload"] = ("llama70b-gqa: 128 requests share a 2048-token prefix; 64 extend 256 tokens (contexts "
                        "2304-8192), 64 decode 1 token (contexts 2049-8192); 64/8 heads, D=128, bf16, 2^20 slots")
     return out
+
+
+def back_to_back_us(fns, steps):
+    """Mean device time of each of `fns` when the sequence is issued `steps`
+    times back to back with no synchronization in between (as the timed step
+    loop issues its calls): HIP events on the launch stream between the
+    calls, one synchronization at the end.  A call whose host side is slower
+    than the kernels before it shows that host time too."""
+    import torch
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps * len(fns) + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    i = 0
+    for _ in range(steps):
+        for f in fns:
+            f()
+            i += 1
+            ev[i].record(stream)
+    torch.cuda.synchronize()
+    t = np.array([ev[j].elapsed_time(ev[j + 1]) for j in range(i)]).reshape(steps, len(fns))
+    return [float(x) * 1e3 for x in t.mean(axis=0)]
 
 
 def graph_replay_us(fn, steps, warmup):
@@ -905,8 +933,10 @@ def main():
                       frac_of_peak_unique=dec_gbs_u / PEAK_HBM_GBS,
                       tokens_per_s=T_d / ((kern_ms[2] + kern_ms[3]) * 1e-3), scatter_us=kern_ms[2] * 1e3,
                       plan=dict(jobs=pl.n_jobs, records=pl.n_records, tail_splits=pl.tail_splits,
-                                max_members=pl.max_members, tail_chunk=pl.tail_chunk, host_ms=dec.plan_ms,
-                                settings="seg_chunk 256, tail_chunk 768, min_keys 32 (the engine's defaults)"))
+                                max_members=pl.max_members, tail_chunk=pl.tail_chunk, seg_chunk=pl.seg_chunk,
+                                host_ms=dec.plan_ms,
+                                settings="the engine's rules: tail_chunk 768 keys (384 for a small grouped-head "
+                                         "launch), seg_chunk = tail_chunk (256 when halved), min_keys 32"))
     pl_us = float(np.mean(pl_ms)) * 1e3
     # plain decode reads every context whole, the shared rows partly from
     # L2/MALL: its logical rate is bytes delivered to the kernel, and its HBM

@@ -878,45 +878,49 @@ __global__ __launch_bounds__(64) void decode_merge(DecodeArgs a) {
   const int lane = threadIdx.x;
   const float* src = ws_row(a, D, r, head, rec0);
   const int64_t stride = a.rec_indptr ? (int64_t)a.hq * (D + 4) : (D + 4);
-  float M = -INFINITY;
-  for (int s = lane; s < nsplit; s += 64) M = fmaxf(M, src[(int64_t)s * stride + D]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   constexpr int PER = D / 64;
-  float acc[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-  float lsum = 0.f;
-  // partials combined in split order; their loads are issued four splits at
-  // a time, so a request waits about one memory latency per four splits
-  // instead of one per split
-  auto add = [&](float ms, float ls, const float (&v)[PER]) {
-    const float f = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-    lsum += ls * f;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) acc[i] += v[i] * f;
-  };
-  constexpr int UNR = 4;
-  int s = 0;
-  for (; s + UNR <= nsplit; s += UNR) {
-    float ms[UNR], ls[UNR], v[UNR][PER];
+  // The partials are combined in split order against their common maximum
+  // M.  They are loaded UNR splits at a time, every load of a group issued
+  // before any is used (an index past the last split reads the last split
+  // again and is not added): a request of up to UNR splits waits one memory
+  // latency for all of them, and its group also gives M.  With more splits
+  // a first pass over the maxima gives M.
+  constexpr int UNR = 8;
+  float ms[UNR], ls[UNR], v[UNR][PER];
+  auto load_group = [&](int s) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      const float* p = src + (int64_t)(s + u) * stride;
+      const float* p = src + (int64_t)min(s + u, nsplit - 1) * stride;
       ms[u] = p[D];
       ls[u] = p[D + 1];
 #pragma unroll
       for (int i = 0; i < PER; ++i) v[u][i] = p[lane + 64 * i];
     }
+  };
+  float M = -INFINITY;
+  if (nsplit <= UNR) {
+    load_group(0);
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) add(ms[u], ls[u], v[u]);
+    for (int u = 0; u < UNR; ++u) M = fmaxf(M, ms[u]);     // indices past the last repeat it
+  } else {
+    for (int s = lane; s < nsplit; s += 64) M = fmaxf(M, src[(int64_t)s * stride + D]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   }
-  for (; s < nsplit; ++s) {
-    const float* p = src + (int64_t)s * stride;
-    float v[PER];
+  float acc[PER];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) v[i] = p[lane + 64 * i];
-    add(p[D], p[D + 1], v);
+  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+  float lsum = 0.f;
+  for (int s = 0; s < nsplit; s += UNR) {
+    if (nsplit > UNR) load_group(s);
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      if (s + u >= nsplit) break;
+      const float f = (ms[u] == -INFINITY) ? 0.f : exp2f(ms[u] - M);
+      lsum += ls[u] * f;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) acc[i] += v[u][i] * f;
+    }
   }
   const float inv = 1.f / lsum;
   const int64_t ooff = ((int64_t)r * a.hq + head) * D;

@@ -209,22 +209,40 @@ class RadixKVCache:
     # such launches are latency-bound, and shorter items finish sooner (one
     # GPU's 8/1 heads of the 64/8 decode batch, 312 tail items at 768 keys:
     # 36.7 -> 33.9 us at 384).
+    # Shared chunk: the tail chunk, so a shared item is no longer than a tail
+    # item and a shared run is cut into as few partial states as that allows
+    # (64/8-head decode under a 2048-key prefix: 207.0 us at 256-key chunks,
+    # 191.2 at 512, 188.5 at 768, 194.4 at 1024; the 32-head tree batch 1135.8
+    # / 1126.7 / 1127.5 us at 256 / 512 / 768).  When the tail chunk is halved
+    # the shared chunk is 256 keys: a shared item computes several requests'
+    # query columns per key and takes longer per step than a tail item, and
+    # in a latency-bound launch the longest item sets the time (the 8/1-head
+    # share: 28.4 us at 256, 29.5 at 192, 32.5 at 384).
     TAIL_CHUNK = 768
     MIN_TAIL_ITEMS = 1024
+    SEG_CHUNK_SMALL = 256
 
-    def cascade_plan(self, batch: Batch, hq, seg_chunk=256, tail_chunk=None, min_keys=32, max_members=None):
+    def cascade_plan(self, batch: Batch, hq, seg_chunk=None, tail_chunk=None, min_keys=32, max_members=None):
         """Plans prefix-shared decode from the batch's host tables and copies
-        the plan to the device.  tail_chunk None: the rule above."""
+        the plan to the device.  seg_chunk / tail_chunk None: the rules
+        above."""
+        return self.cascade_plan_host(batch, hq, seg_chunk, tail_chunk, min_keys, max_members).to(self.device)
+
+    def cascade_plan_host(self, batch: Batch, hq, seg_chunk=None, tail_chunk=None, min_keys=32, max_members=None):
+        """The host plan of cascade_plan, before its copy to the device."""
         mm = rkv.cascade_max_members(hq, self.hkv, self.d) if max_members is None else max_members
         tc = self.TAIL_CHUNK if tail_chunk is None else tail_chunk
-        args = (batch.host["req_to_token"], batch.host["seq_lens"], seg_chunk, tc, min_keys, mm)
-        plan = rkv.cascade_plan(*args)
+        sc = tc if seg_chunk is None else seg_chunk
+        rows, lens = batch.host["req_to_token"], batch.host["seq_lens"]
+        plan = rkv.cascade_plan(rows, lens, sc, tc, min_keys, mm)
         if tail_chunk is None and hq // self.hkv >= 4:
-            tails = batch.host["seq_lens"].astype(np.int64) - plan.tail_begin
+            # where the tails start does not depend on either chunk
+            tails = lens.astype(np.int64) - plan.tail_begin
             items = int(((tails + tc - 1) // tc).sum()) * self.hkv
             if 0 < items < self.MIN_TAIL_ITEMS:
-                plan = rkv.cascade_plan(*args[:3], tc // 2, *args[4:])
-        return plan.to(self.device)
+                sc = self.SEG_CHUNK_SMALL if seg_chunk is None else seg_chunk
+                plan = rkv.cascade_plan(rows, lens, sc, tc // 2, min_keys, mm)
+        return plan
 
     def decode_cascade(self, batch: Batch, q, plan=None, o=None, lse=None, stream=None, **plan_args):
         """Decode that reads each run of keys shared by several requests of

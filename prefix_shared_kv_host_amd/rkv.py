@@ -467,11 +467,13 @@ def attn_decode_noalloc(q, k_pool, v_pool, o, req_to_token, seq_lens, max_seq_le
 class CascadePlan:
     """Host arrays of a prefix-shared decode plan (rkv_cascade_plan):
     perm [B], rec_indptr [B+1], tail_begin [B], jobs [n_jobs, 5] (int32
-    NumPy), with tail_splits, n_records, max_members and tail_chunk."""
+    NumPy), with tail_splits, n_records, max_members, tail_chunk and the
+    seg_chunk it was planned with (host information only)."""
 
-    def __init__(self, perm, rec_indptr, tail_begin, jobs, tail_splits, max_members, tail_chunk):
+    def __init__(self, perm, rec_indptr, tail_begin, jobs, tail_splits, max_members, tail_chunk, seg_chunk=None):
         self.perm, self.rec_indptr, self.tail_begin, self.jobs = perm, rec_indptr, tail_begin, jobs
         self.tail_splits, self.max_members, self.tail_chunk = int(tail_splits), int(max_members), int(tail_chunk)
+        self.seg_chunk = None if seg_chunk is None else int(seg_chunk)
         self.n_records = int(rec_indptr[-1])
         self.n_jobs = int(jobs.shape[0])
         self.dev = None
@@ -526,7 +528,7 @@ def cascade_plan(req_to_token, seq_lens, seg_chunk=256, tail_chunk=768, min_keys
         jobs = np.empty((n_jobs.value, 5), dtype=np.int32)
         code = lib().rkv_cascade_plan(*args(jobs.ctypes.data_as(c_i32p), n_jobs.value))
     _check(code)
-    return CascadePlan(perm[:B], rec, tb[:B], jobs[: n_jobs.value], tail.value, max_members, tail_chunk)
+    return CascadePlan(perm[:B], rec, tb[:B], jobs[: n_jobs.value], tail.value, max_members, tail_chunk, seg_chunk)
 
 
 def attn_decode_cascade_workspace_bytes(n_records, hq, d) -> int:

@@ -158,22 +158,28 @@ def run(shape, phases, select=lambda i, B: None, num_splits=None, content_device
     return out, cache
 
 
-def check_plan(plan, otb, seg_chunk=256, tail_chunk=None, min_keys=32, max_members=None, hkv=None, G=None):
+def check_plan(plan, otb, seg_chunk=None, tail_chunk=None, min_keys=32, max_members=None, hkv=None, G=None):
     """The native prefix-shared plan equals the oracle's, array by array.
     tail_chunk None: the engine's default rule, 768 keys, or 384 when the
-    grouped-head tails (G >= 4) would give fewer than 1024 items at 768."""
+    grouped-head tails (G >= 4) would give fewer than 1024 items at 768.
+    seg_chunk None: the tail chunk, or 256 keys when the rule halved it."""
     from oracle import cascade as ocas
     L = otb["seq_lens"]
+    sc = seg_chunk
     if tail_chunk is None:
         tail_chunk = 768
         if G is not None and G >= 4:
             rows = [row[: int(L[r])] for r, row in enumerate(otb["req_to_token"])]
-            first = ocas.plan(rows, L, seg_chunk, 768, min_keys, plan.max_members)
+            first = ocas.plan(rows, L, 768, 768, min_keys, plan.max_members)
             tails = np.asarray(L, dtype=np.int64) - np.asarray(first["tail_begin"], dtype=np.int64)
             items = int(((tails + 767) // 768).sum()) * hkv
             if 0 < items < 1024:
                 tail_chunk = 384
+                sc = 256 if seg_chunk is None else seg_chunk
         assert plan.tail_chunk == tail_chunk, (plan.tail_chunk, tail_chunk)
+    seg_chunk = tail_chunk if sc is None else sc
+    if plan.seg_chunk is not None:
+        assert plan.seg_chunk == seg_chunk, (plan.seg_chunk, seg_chunk)
     ref = ocas.plan([row[: int(L[r])] for r, row in enumerate(otb["req_to_token"])], L, seg_chunk,
                     tail_chunk, min_keys, plan.max_members)
     assert plan.perm.tolist() == ref["perm"]

@@ -74,3 +74,41 @@ def test_plain_decode_splits_rule():
     ns = splits_for(8, 1, [2000] * 8)
     assert ns == 2000 // 256 and ns > -(-2000 // 768)
     assert splits_for(8, 1, []) == 0
+
+
+def plan_for(hkv, hq, lens, shared=2048, **kw):
+    """The engine's host plan for requests whose first `shared` keys are one
+    run of slots and whose other keys are private."""
+    from types import SimpleNamespace
+    c = RadixKVCache.__new__(RadixKVCache)      # the rule needs no pool
+    c.hkv, c.d = hkv, 128
+    lens = np.asarray(lens, dtype=np.int32)
+    ld = int(lens.max())
+    rows = np.zeros((len(lens), ld), dtype=np.int32)
+    nxt = shared
+    for r, n in enumerate(lens):
+        rows[r, :shared] = np.arange(shared)
+        rows[r, shared:n] = np.arange(nxt, nxt + n - shared)
+        nxt += n - shared
+    b = SimpleNamespace(host={"req_to_token": rows, "seq_lens": lens})
+    return c.cascade_plan_host(b, hq, **kw), rows, lens
+
+
+def test_cascade_chunk_rule():
+    """The prefix-shared plan cuts shared runs into chunks of the tail chunk
+    (768 keys), and into 256-key chunks when the tail chunk is halved for a
+    launch of fewer than 1024 grouped-head tail items; chunks given by the
+    caller are kept.  The plan is the planner's own for the chosen chunks."""
+    from prefix_shared_kv_host_amd import rkv
+    lens = np.random.default_rng(7).integers(2049, 8193, 64)
+    for hkv, hq, tc, sc in ((8, 64, 768, 768), (1, 8, 384, 256), (32, 32, 768, 768), (1, 1, 768, 768)):
+        p, rows, L = plan_for(hkv, hq, lens)
+        assert (p.tail_chunk, p.seg_chunk) == (tc, sc), (hkv, hq)
+        ref = rkv.cascade_plan(rows, L, sc, tc, 32, rkv.cascade_max_members(hq, hkv, 128))
+        for k in ("perm", "rec_indptr", "tail_begin", "jobs"):
+            assert np.array_equal(getattr(p, k), getattr(ref, k)), (hkv, hq, k)
+        assert p.n_jobs and int((p.jobs[:, 1] - p.jobs[:, 0]).max()) <= sc
+        assert np.all(p.tail_begin == 2048)
+        q, _, _ = plan_for(hkv, hq, lens, seg_chunk=100)
+        assert q.seg_chunk == 100 and q.tail_chunk == tc
+        assert np.array_equal(q.tail_begin, p.tail_begin)    # where tails start depends on neither chunk
