@@ -464,14 +464,22 @@ size_t rkv_attn_decode_cascade_workspace_bytes(int64_t n_records, int32_t hq, in
  * a job or request that does not fit is skipped, and with RKV_DEBUG=1 the
  * call returns RKV_EINVAL.  Workspace: rkv_attn_decode_cascade_workspace_bytes
  * (may be NULL when n_jobs == 0 and n_records == B: every request then has
- * one partial). */
+ * one partial).
+ * tail_order (nullable, int32 [B], device): a permutation of the requests
+ * in which the tail splits are handed out (the shared jobs keep the plan's
+ * order); it changes only the schedule (every output is bit-identical to
+ * NULL's).  Requests whose tail splits are longest first let the launch end
+ * on short items.  An entry outside [0, B) is skipped; a repeated or missing
+ * request leaves its tails computed twice or not at all (its output then
+ * merges stale workspace). */
 int rkv_attn_decode_cascade(const void* q, const void* k_pool, const void* v_pool, void* o, float* lse,
                             const int32_t* req_to_token, int64_t ld, const int32_t* seq_lens, int32_t B,
                             int32_t max_seq_len, int32_t hq, int32_t hkv, int32_t d, float sm_scale,
                             int32_t dtype, const int32_t* perm, const int32_t* rec_indptr,
                             const int32_t* tail_begin, const int32_t* jobs, int64_t n_jobs,
-                            int32_t max_members, int32_t tail_chunk, int32_t tail_splits, int64_t n_records,
-                            void* workspace, size_t ws_bytes, int64_t pool_slots, void* stream);
+                            const int32_t* tail_order, int32_t max_members, int32_t tail_chunk,
+                            int32_t tail_splits, int64_t n_records, void* workspace, size_t ws_bytes,
+                            int64_t pool_slots, void* stream);
 
 /* ------------------------------------------------------------------------
  * Sampling penalties over the running requests (the sampling page,

@@ -67,6 +67,9 @@ struct DecodeArgs {
   const int32_t* tail_begin;
   int32_t n_records;
   int32_t tail_chunk;
+  // optional order of the requests' tail splits (null: batch order): the
+  // tail item at request position i works on request tail_order[i]
+  const int32_t* tail_order;
 };
 
 // Prefix-shared jobs: keys [key_begin, key_end) of request perm[first]'s row
@@ -490,9 +493,13 @@ __device__ __forceinline__ void gqa_item(const DecodeArgs& a, int64_t w, char* V
   using namespace gqa;
   const int s = (int)(w % a.splits);
   int64_t rest = w / a.splits;
-  const int r = (int)(rest % a.B);
+  int r = (int)(rest % a.B);
   const int g = (int)(rest / a.B);
   if (g >= a.hkv) return;
+  if (a.tail_order) {
+    r = a.tail_order[r];
+    if ((unsigned)r >= (unsigned)a.B) return;
+  }
   const int L = min(a.seq_lens[r], a.max_seq_len);
   int k_begin, k_end, rec, nsplit;
   if (!split_span(a, r, s, L, k_begin, k_end, rec, nsplit)) return;
@@ -656,11 +663,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CB > 0 ? 2 
   // so neighbouring requests (siblings in the tree) share an XCD
   const int s = (int)(w % a.splits);
   int64_t rest = w / a.splits;
-  const int r = (int)(rest % a.B);
+  int r = (int)(rest % a.B);
   rest /= a.B;
   const int sub = (int)(rest % a.hg);
   const int hblk = (int)(rest / a.hg);
   if (hblk * HB >= a.hkv) return;
+  if (a.tail_order) {
+    r = a.tail_order[r];
+    if ((unsigned)r >= (unsigned)a.B) return;
+  }
   const int L = min(a.seq_lens[r], a.max_seq_len);
   int k_begin, k_end, rec, nsplit;
   if (!split_span(a, r, s, L, k_begin, k_end, rec, nsplit)) return;
@@ -1064,6 +1075,7 @@ int decode_launch(const char* who, const void* q, const void* k_pool, const void
   a.tail_begin = nullptr;
   a.n_records = 0;
   a.tail_chunk = 0;
+  a.tail_order = nullptr;
   a.err = flag;
   int64_t grid = (int64_t)S * B * ((hkv + a.hb - 1) / a.hb) * a.hg;
   grid = (grid + rkv::kXcds - 1) / rkv::kXcds * rkv::kXcds;
@@ -1191,7 +1203,8 @@ extern "C" int rkv_attn_decode_cascade(const void* q, const void* k_pool, const 
                                        int32_t hkv, int32_t d, float sm_scale, int32_t dtype,
                                        const int32_t* perm, const int32_t* rec_indptr,
                                        const int32_t* tail_begin, const int32_t* jobs, int64_t n_jobs,
-                                       int32_t max_members, int32_t tail_chunk, int32_t tail_splits,
+                                       const int32_t* tail_order, int32_t max_members, int32_t tail_chunk,
+                                       int32_t tail_splits,
                                        int64_t n_records, void* workspace, size_t ws_bytes,
                                        int64_t pool_slots, void* stream) {
   rkv::clear_error();
@@ -1233,6 +1246,7 @@ extern "C" int rkv_attn_decode_cascade(const void* q, const void* k_pool, const 
   a.tail_begin = tail_begin;
   a.n_records = (int32_t)n_records;
   a.tail_chunk = tail_chunk;
+  a.tail_order = tail_order;
   if (int rc = rkv::debug_flag(&a.err)) return rc;
   SharedJobs j;
   j.jobs = jobs;

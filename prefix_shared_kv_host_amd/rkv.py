@@ -116,8 +116,8 @@ def lib():
                                             c_i32p, c_i32p, c_i32p, _i64, c_i64p, c_i32p]),
         "rkv_attn_decode_cascade_workspace_bytes": (_sz, [_i64, _i32, _i32]),
         "rkv_attn_decode_cascade": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32, _i32, _i32,
-                                                   _i32, _i32, _f32, _i32, _vp, _vp, _vp, _vp, _i64, _i32,
-                                                   _i32, _i32, _i64, _vp, _sz, _i64, _vp]),
+                                                   _i32, _i32, _f32, _i32, _vp, _vp, _vp, _vp, _i64, _vp,
+                                                   _i32, _i32, _i32, _i64, _vp, _sz, _i64, _vp]),
         "rkv_image_keys": (ctypes.c_int, [ctypes.c_char_p, _i64, _i64, c_i32p, ctypes.POINTER(ctypes.c_uint64)]),
         "rkv_penalty_admit": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
         "rkv_penalty_accumulate": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
@@ -468,12 +468,15 @@ class CascadePlan:
     """Host arrays of a prefix-shared decode plan (rkv_cascade_plan):
     perm [B], rec_indptr [B+1], tail_begin [B], jobs [n_jobs, 5] (int32
     NumPy), with tail_splits, n_records, max_members, tail_chunk and the
-    seg_chunk it was planned with (host information only)."""
+    seg_chunk it was planned with (host information only).  tail_order
+    (int32 [B] or None): the order in which rkv_attn_decode_cascade hands
+    out the requests' tail splits (None: batch order)."""
 
     def __init__(self, perm, rec_indptr, tail_begin, jobs, tail_splits, max_members, tail_chunk, seg_chunk=None):
         self.perm, self.rec_indptr, self.tail_begin, self.jobs = perm, rec_indptr, tail_begin, jobs
         self.tail_splits, self.max_members, self.tail_chunk = int(tail_splits), int(max_members), int(tail_chunk)
         self.seg_chunk = None if seg_chunk is None else int(seg_chunk)
+        self.tail_order = None
         self.n_records = int(rec_indptr[-1])
         self.n_jobs = int(jobs.shape[0])
         self.dev = None
@@ -487,6 +490,8 @@ class CascadePlan:
         import torch
         parts = (("perm", self.perm), ("rec_indptr", self.rec_indptr), ("tail_begin", self.tail_begin),
                  ("jobs", self.jobs.reshape(-1)))
+        if self.tail_order is not None:
+            parts += (("tail_order", np.asarray(self.tail_order, dtype=np.int32)),)
         spans, off = {}, 0
         for k, v in parts:
             spans[k] = (off, int(v.size))
@@ -551,7 +556,8 @@ def attn_decode_cascade(q, k_pool, v_pool, o, req_to_token, seq_lens, max_seq_le
         _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(o), _ptr(lse), _ptr(req_to_token),
         int(req_to_token.shape[1]), _ptr(seq_lens), int(B), int(max_seq_len), int(hq), int(hkv), int(d),
         scale, _dtype_code(q), _ptr(dv["perm"]), _ptr(dv["rec_indptr"]), _ptr(dv["tail_begin"]),
-        _ptr(dv["jobs"]) if plan.n_jobs else None, plan.n_jobs, plan.max_members, plan.tail_chunk,
+        _ptr(dv["jobs"]) if plan.n_jobs else None, plan.n_jobs,
+        _ptr(dv["tail_order"]) if "tail_order" in dv else None, plan.max_members, plan.tail_chunk,
         plan.tail_splits, plan.n_records, _ptr(workspace), int(ws_bytes), int(P), _stream(stream)))
 
 

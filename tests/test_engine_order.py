@@ -112,3 +112,37 @@ def test_cascade_chunk_rule():
         q, _, _ = plan_for(hkv, hq, lens, seg_chunk=100)
         assert q.seg_chunk == 100 and q.tail_chunk == tc
         assert np.array_equal(q.tail_begin, p.tail_begin)    # where tails start depends on neither chunk
+
+
+def test_cascade_tail_order():
+    """The prefix-shared plan hands out the requests' tail splits longest
+    first (split length as the kernels cut it: the tail in ceil(tail /
+    tail_chunk) equal splits rounded up to 64 keys, never above tail_chunk),
+    ties in batch order, when each XCD's contiguous range of tail items is
+    whole head blocks (64/8 and 32/32 heads); otherwise (one kv head) the
+    sorted requests are dealt over the 8 ranges, each longest first and of
+    about equal total.  Off on request, for a single request and for
+    launches of fewer than 1024 tail items (the 8/1-head share)."""
+    lens = np.random.default_rng(11).integers(2049, 8193, 64)
+    small, _, _ = plan_for(1, 8, lens)
+    assert small.tail_chunk == 384 and small.tail_order is None
+    for hkv, hq, whole, B in ((8, 64, True, 64), (1, 8, False, 512), (32, 32, True, 64)):
+        lens = np.random.default_rng(11).integers(2049, 8193, B)
+        p, _, L = plan_for(hkv, hq, lens)
+        o = p.tail_order
+        assert o is not None and sorted(o.tolist()) == list(range(len(L)))
+        tails = L.astype(np.int64) - p.tail_begin
+        n = -(-tails // p.tail_chunk)
+        split = np.minimum(np.minimum(-(-(-(-tails // n)) // 64) * 64, p.tail_chunk), tails)
+        runs = [o] if whole else np.array_split(o, 8)
+        for run in runs:
+            for i in range(len(run) - 1):
+                a, b = split[run[i]], split[run[i + 1]]
+                assert a > b or (a == b and run[i] < run[i + 1])
+        if not whole:
+            sums = [int(split[run].sum()) for run in runs]
+            assert max(sums) - min(sums) <= int(split.max())
+        off, _, _ = plan_for(hkv, hq, lens, longest_tails_first=False)
+        assert off.tail_order is None
+    one, _, _ = plan_for(8, 64, lens[:1])
+    assert one.tail_order is None

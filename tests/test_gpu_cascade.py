@@ -108,3 +108,63 @@ def test_cascade_c4_decode_sampled():
     ph = [phases[0], phases[1], phases[3]]
     res, _ = G.run(shape, ph, select=G.sample(6, 16), sparse=True, cascade={})
     G.check(res, "bf16", "c4-decode cascade")
+
+
+ORDER_CASES = [
+    # hq, hkv, d: tails on the vector kernel, on the matrix cores, and a
+    # small grouped-head launch (halved tail chunk)
+    (32, 32, 128),
+    (32, 8, 128),
+    (8, 1, 64),
+]
+
+
+@pytest.mark.timeout(400)
+@pytest.mark.parametrize("hq,hkv,d", ORDER_CASES)
+def test_cascade_tail_order_changes_only_the_schedule(hq, hkv, d):
+    """The order in which the tail splits are handed out (the engine's
+    longest-first order, batch order, a reversed order) changes no output
+    bit; an order entry outside [0, B) is skipped without touching the
+    other requests' outputs."""
+    from inputs import content
+    shape = configs.Shape(f"cas-order-{hq}-{hkv}-{d}", hq, hkv, d, "bf16", 1 << 17, 91)
+    phases = tree_decode_workload(seed=hq + hkv + d, B=48, max_len=2500)
+    res, cache = G.run(shape, phases, content_device="cpu", cascade={}, select=G.sample(2, 8), sparse=True)
+    G.check(res, "bf16", f"cascade tail order {hq}/{hkv} d{d}")
+    (r,) = res
+    b = r["batch"]
+    seqs = phases[-1].seqs
+    B = len(seqs)
+    q, _, _ = content.batch_rows(shape.seed, seqs, b.host["prefix_lens"], hq, hkv, d, torch.bfloat16, "cuda",
+                                 shape.q_scale)
+    eng = cache.cascade_plan_host(b, hq)
+    # the engine's order (a small launch keeps batch order: then requests by
+    # length, longest first)
+    base = eng.tail_order
+    if base is None:
+        base = np.argsort(-b.host["seq_lens"].astype(np.int64), kind="stable").astype(np.int32)
+    assert sorted(base.tolist()) == list(range(B))
+
+    def decode(order):
+        p = cache.cascade_plan_host(b, hq, longest_tails_first=False)
+        assert p.tail_order is None
+        p.tail_order = None if order is None else np.asarray(order, dtype=np.int32)
+        p.to("cuda")
+        o = torch.empty_like(q)
+        lse = torch.empty(B, hq, dtype=torch.float32, device="cuda")
+        cache.decode_cascade(b, q, plan=p, o=o, lse=lse)
+        torch.cuda.synchronize()
+        return o.view(torch.int16).cpu(), lse.view(torch.int32).cpu()
+
+    ref = decode(base)
+    assert torch.equal(ref[0], r["o_full"].view(torch.int16).cpu())
+    for order in (None, np.arange(B)[::-1]):
+        out = decode(order)
+        assert torch.equal(out[0], ref[0]) and torch.equal(out[1], ref[1])
+    bad = base.copy()
+    victim = int(bad[0])
+    bad[0] = B + 5
+    out = decode(bad)
+    keep = torch.ones(B, dtype=torch.bool)
+    keep[victim] = False
+    assert torch.equal(out[0][keep], ref[0][keep]) and torch.equal(out[1][keep], ref[1][keep])
