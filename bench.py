@@ -783,8 +783,8 @@ def main():
                          "decode; prints one JSON line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this path has no sharding or collectives "
-              "(see DESIGN.md for how it would shard).", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: this path has no sharding or collectives; "
+              "--gpus above 1 is not supported.", file=sys.stderr)
         sys.exit(2)
 
     import torch
